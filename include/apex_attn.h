@@ -1,0 +1,128 @@
+/*
+ * apex_attn.h -- C ABI of the MI355X (gfx950) RoPE + attention library.
+ *
+ * The operations follow the APEX-1 Mathematical Reference:
+ *   - Rotary position embedding (Part 1, §4.2 "Core Idea", §4.3 "Frequency
+ *     Formula", §4.4 "Compact Form"): the pair (x_2i, x_2i+1) of a head vector
+ *     at position p is rotated by the angle p*theta_i, theta_i = b^(-2i/d_h):
+ *       x'_2i   = x_2i cos(p theta_i) - x_2i+1 sin(p theta_i)
+ *       x'_2i+1 = x_2i sin(p theta_i) + x_2i+1 cos(p theta_i)
+ *   - Scaled dot-product attention (Part 2, §6.2):
+ *       Attention(Q, K, V) = softmax(Q K^T / sqrt(d_h)) V
+ *   - Grouped-query attention (Part 2, §8.2): G = H_q / H_kv and query head h
+ *     reads KV head floor(h / G).
+ *   - Causal and sliding-window masks (Part 2, §10.2): key j is visible to
+ *     query i iff j <= i and, when W > 0, i - j < W (W keys including i).
+ *
+ * Conventions shared by every call:
+ *   - Tensors are contiguous row-major [B, H, S, d_h] (Part 1, §1 "Tensor
+ *     Shape Convention"): element (b, h, s, t) sits at ((b*H + h)*S + s)*d_h + t.
+ *   - dtype: APEX_F32 (fp32 storage and math) or APEX_BF16 (bf16 storage,
+ *     fp32 softmax and accumulation, bf16 output rounded to nearest even).
+ *   - Every pointer is a device pointer owned by the caller, 16-byte aligned.
+ *     The library never allocates, frees or synchronizes; it keeps no mutable
+ *     global state and is reentrant.
+ *   - stream is a hipStream_t (NULL = the null stream). Every call only
+ *     enqueues work on it and returns; results are ready when the stream is.
+ *   - Every call checks all of its arguments before enqueueing anything. On a
+ *     bad argument it returns a negative apex_status and enqueues nothing.
+ *     A failed kernel launch returns APEX_EHIP. No C++ exception crosses the ABI.
+ *   - Supported head sizes: d_h = 64 or 128 (other even sizes return
+ *     APEX_EUNSUPPORTED, odd sizes APEX_EINVAL).
+ */
+#ifndef APEX_ATTN_H
+#define APEX_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  APEX_OK = 0,
+  APEX_EINVAL = -1,        /* a size, pointer, flag or position is invalid   */
+  APEX_EUNSUPPORTED = -2,  /* valid by the definition, not built (d_h, dtype) */
+  APEX_EWORKSPACE = -3,    /* decode workspace missing or too small          */
+  APEX_EHIP = -4           /* the HIP runtime reported a launch error        */
+} apex_status;
+
+enum { APEX_F32 = 0, APEX_BF16 = 1 };
+
+/*
+ * apex_rope_qk -- rotate Q and K in place (Part 1, §4.2-§4.4).
+ *   q: [B, H_q, S, d_h], rotated in place; row s sits at position m0 + s.
+ *   k: [B, H_kv, S, d_h], rotated in place at the same positions, or NULL.
+ *   base: the RoPE base b (> 0), 10000 on the pages.
+ * Angles are formed in fp64 and reduced to one turn before the fp32 sine and
+ * cosine, so positions up to 2^31 keep full fp32 accuracy.
+ * Errors: APEX_EINVAL for B, S, H_q < 1, H_kv < 1 when k is given, m0 < 0,
+ * base <= 0, q == NULL, or an unknown dtype.
+ */
+int apex_rope_qk(void* q, void* k, int B, int S, int H_q, int H_kv, int d_h,
+                 int64_t m0, double base, int dtype, void* stream);
+
+/*
+ * apex_attn_prefill -- o = softmax(RoPE(q) RoPE(k)^T / sqrt(d_h)) v with GQA
+ * and the causal / window mask (Part 2, §6.2, §8.2, §10.2).
+ *   q: [B, H_q, S, d_h]   (read only)
+ *   k: [B, H_kv, S, d_h]  (read only)
+ *   v: [B, H_kv, S, d_h]  (read only)
+ *   o: [B, H_q, S, d_h]   output; must not overlap any input.
+ *   causal: 1 = key j visible to query i only if j <= i; 0 = all visible.
+ *   W: window width (> 0 requires causal = 1); 0 = no window.
+ *   m0: position of row 0 (>= 0). The mask depends on i - j only.
+ *   apply_rope: 1 = q and k are raw: q is rotated while its tiles load and k
+ *     is rotated once into k_rope_out, which the attention then reads;
+ *     0 = q and k already hold rotated values, k_rope_out is ignored.
+ *   k_rope_out: [B, H_kv, S, d_h] receives RoPE(k) when apply_rope = 1 (the
+ *     values a KV cache stores). It may equal k (in-place rotation) but must
+ *     not overlap q, v or o.
+ * Errors: APEX_EINVAL for H_q % H_kv != 0, sizes < 1, W < 0, W > 0 with
+ * causal = 0, m0 < 0, base <= 0 with apply_rope, a NULL required pointer, an
+ * unknown dtype; APEX_EUNSUPPORTED for d_h not 64 or 128.
+ */
+int apex_attn_prefill(const void* q, const void* k, const void* v, void* o,
+                      void* k_rope_out, int B, int S, int H_q, int H_kv, int d_h,
+                      int causal, int W, int64_t m0, double base, int apply_rope,
+                      int dtype, void* stream);
+
+/*
+ * apex_attn_decode_workspace_bytes -- bytes of scratch apex_attn_decode needs
+ * for these sizes (the split-K partial results: per query head and split, a
+ * running max, a sum and d_h fp32 accumulators). Returns 0 for invalid sizes.
+ */
+size_t apex_attn_decode_workspace_bytes(int B, int H_q, int H_kv, int Sk, int d_h);
+
+/*
+ * apex_attn_decode -- one query token per (b, h) at position m against a
+ * cache of Sk slots (Part 2, §6.2 with S_q = 1, §7.4 "KV Cache Problem",
+ * §8.2 GQA, §10.2 window).
+ *   q: [B, H_q, 1, d_h] raw query of the new token (rotated at m if apply_rope).
+ *   k_cache, v_cache: [B, H_kv, Sk, d_h]; slot j holds position j, keys
+ *     stored already rotated. Visible slots: j <= m and (W == 0 or m - j < W).
+ *   k_new, v_new: [B, H_kv, 1, d_h] key and value of the new token, or both
+ *     NULL. When given, the rotated k_new (raw when apply_rope = 0) and v_new
+ *     are written into slot m of the caches and used for slot m in this call.
+ *   o: [B, H_q, 1, d_h] output.
+ *   workspace: device scratch of workspace_bytes >= the value returned by
+ *     apex_attn_decode_workspace_bytes for the same sizes.
+ * Errors: APEX_EINVAL for H_q % H_kv != 0, sizes < 1, W < 0, m < 0 or
+ * m >= Sk, exactly one of k_new / v_new given, base <= 0 with apply_rope, a
+ * NULL required pointer, an unknown dtype; APEX_EUNSUPPORTED for d_h not 64
+ * or 128 or dtype fp32; APEX_EWORKSPACE when workspace is NULL or too small.
+ */
+int apex_attn_decode(const void* q, void* k_cache, void* v_cache,
+                     const void* k_new, const void* v_new, void* o,
+                     int B, int Sk, int H_q, int H_kv, int d_h, int W, int64_t m,
+                     double base, int apply_rope, void* workspace,
+                     size_t workspace_bytes, int dtype, void* stream);
+
+/* apex_strerror -- static text for a status code; never NULL. */
+const char* apex_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* APEX_ATTN_H */

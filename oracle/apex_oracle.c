@@ -1,0 +1,306 @@
+/*
+ * apex_oracle.c -- plain, slow, fp64 CPU oracle for rotary position embedding
+ * followed by scaled dot-product attention with grouped-query KV sharing,
+ * causal masking and sliding-window masking.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg load this library. It shares no code, header or table with
+ * the GPU library, and the GPU library never calls it.
+ *
+ * What it computes, and where that is defined (APEX-1 Mathematical Reference):
+ *   - RoPE frequencies: theta_i = b^(-2i/d_h), i = 0 .. d_h/2-1
+ *     (Part 1, §4.3 "Frequency Formula").
+ *   - RoPE rotation: the pair (x_2i, x_2i+1) is rotated by the angle m*theta_i,
+ *     x'_2i = x_2i cos - x_2i+1 sin,  x'_2i+1 = x_2i sin + x_2i+1 cos
+ *     (Part 1, §4.2 "Core Idea"; the sign and the adjacent pairing are fixed by
+ *     the rotate-half definition of §4.4 and the worked example of §4.6).
+ *   - Attention(Q,K,V) = softmax(Q K^T / sqrt(d_h)) V  (Part 2, §6.2).
+ *   - GQA: G = H_q/H_kv, query head h reads KV head floor(h/G)  (Part 2, §8.2).
+ *   - Window mask: key j is visible to query i iff 0 <= i-j < W and j <= i
+ *     (Part 2, §10.2). W = 0 means no window. Non-causal: every key visible.
+ *
+ * Readings taken where the pages leave a step open:
+ *   - Prefill row s of Q and K sits at position m0 + s; the mask uses i - j only.
+ *   - Decode: the query sits at position m; cache slot j holds position j and
+ *     is stored already rotated; when a new key/value is given it occupies
+ *     slot m (the new key is rotated at m here, the new value used as is).
+ *   - The max subtraction inside the softmax is only for range; it does not
+ *     change the mathematical result.
+ *   - Inputs are read exactly as the device sees them (fp32, or bf16 bits
+ *     widened exactly) and every intermediate is fp64 with no rounding.
+ *
+ * Build: gcc -O2 -shared -fPIC -pthread apex_oracle.c -lm
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+
+/* Exact widening of one stored element to double. */
+static double load_elem(const void* base, int dtype, int64_t idx) {
+  if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* theta_i = b^(-2i/d_h)  (Part 1, §4.3). */
+int apex_oracle_theta(int d_h, double base, double* theta) {
+  if (d_h < 2 || (d_h & 1) || !(base > 0.0) || !theta) return -1;
+  for (int i = 0; i < d_h / 2; i++) theta[i] = pow(base, -2.0 * i / d_h);
+  return 0;
+}
+
+/* Rotate one row x[0..d_h) at position pos into y (y may equal x)  (Part 1, §4.2). */
+void apex_oracle_rope_row(const double* x, double* y, int d_h, int64_t pos, double base) {
+  for (int i = 0; i < d_h / 2; i++) {
+    double theta = pow(base, -2.0 * i / d_h);
+    double angle = (double)pos * theta;
+    double c = cos(angle), s = sin(angle);
+    double a = x[2 * i], b = x[2 * i + 1];
+    y[2 * i] = a * c - b * s;
+    y[2 * i + 1] = a * s + b * c;
+  }
+}
+
+/* Visibility of key j to query i  (Part 2, §10.2; causal = j <= i). */
+int apex_oracle_visible(int64_t i, int64_t j, int causal, int64_t W) {
+  if (!causal) return 1;
+  if (j > i) return 0;
+  if (W > 0 && !(i - j < W)) return 0;
+  return 1;
+}
+
+/* softmax(q.k_j * scale) over the n listed keys, then the weighted sum of v_j.
+ * keys[j], vals[j] point at rows of length d. probs (optional) receives the
+ * n weights.  (Part 2, §6.2) */
+static void attend(const double* q, const double* const* keys, const double* const* vals,
+                   int64_t n, int d, double scale, double* scores, double* out, double* probs) {
+  double mx = -INFINITY;
+  for (int64_t j = 0; j < n; j++) {
+    double dot = 0.0;
+    for (int t = 0; t < d; t++) dot += q[t] * keys[j][t];
+    scores[j] = dot * scale;
+    if (scores[j] > mx) mx = scores[j];
+  }
+  double sum = 0.0;
+  for (int64_t j = 0; j < n; j++) {
+    scores[j] = exp(scores[j] - mx);
+    sum += scores[j];
+  }
+  for (int t = 0; t < d; t++) out[t] = 0.0;
+  for (int64_t j = 0; j < n; j++) {
+    double w = scores[j] / sum;
+    if (probs) probs[j] = w;
+    for (int t = 0; t < d; t++) out[t] += w * vals[j][t];
+  }
+}
+
+/* ---- a minimal parallel-for over [0, n) ---- */
+typedef void (*range_fn)(void* ctx, int64_t lo, int64_t hi);
+typedef struct { range_fn fn; void* ctx; int64_t lo, hi; } range_job;
+static void* range_thread(void* p) {
+  range_job* j = (range_job*)p;
+  j->fn(j->ctx, j->lo, j->hi);
+  return NULL;
+}
+static void parallel_for(int64_t n, int nthreads, range_fn fn, void* ctx) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if ((int64_t)nthreads > n) nthreads = (int)(n > 0 ? n : 1);
+  if (nthreads == 1) { fn(ctx, 0, n); return; }
+  pthread_t th[256];
+  range_job jobs[256];
+  for (int t = 0; t < nthreads; t++) {
+    jobs[t].fn = fn; jobs[t].ctx = ctx;
+    jobs[t].lo = n * t / nthreads; jobs[t].hi = n * (t + 1) / nthreads;
+    pthread_create(&th[t], NULL, range_thread, &jobs[t]);
+  }
+  for (int t = 0; t < nthreads; t++) pthread_join(th[t], NULL);
+}
+
+/* ---------------------------- prefill ---------------------------- */
+typedef struct {
+  const void *q, *k, *v;
+  int dtype, S, Hq, Hkv, d, causal, W, apply_rope;
+  int64_t m0;
+  double base;
+  int b, kvh;
+  double *krot, *vd;          /* [S, d] rotated keys and widened values of the group */
+  const int64_t* rows;        /* requested flat rows of this group */
+  const int64_t* row_slot;    /* where each requested row goes in out */
+  double* out;
+  double* probs;              /* optional [nrows, S] */
+} prefill_ctx;
+
+static void prefill_prepare_keys(void* p, int64_t lo, int64_t hi) {
+  prefill_ctx* c = (prefill_ctx*)p;
+  int64_t kv_off = ((int64_t)c->b * c->Hkv + c->kvh) * c->S;
+  for (int64_t j = lo; j < hi; j++) {
+    double* kr = c->krot + j * c->d;
+    double* vr = c->vd + j * c->d;
+    for (int t = 0; t < c->d; t++) {
+      kr[t] = load_elem(c->k, c->dtype, (kv_off + j) * c->d + t);
+      vr[t] = load_elem(c->v, c->dtype, (kv_off + j) * c->d + t);
+    }
+    if (c->apply_rope) apex_oracle_rope_row(kr, kr, c->d, c->m0 + j, c->base);
+  }
+}
+
+static void prefill_rows(void* p, int64_t lo, int64_t hi) {
+  prefill_ctx* c = (prefill_ctx*)p;
+  double* q = (double*)malloc(sizeof(double) * c->d);
+  double* scores = (double*)malloc(sizeof(double) * c->S);
+  const double** keys = (const double**)malloc(sizeof(double*) * c->S);
+  const double** vals = (const double**)malloc(sizeof(double*) * c->S);
+  int64_t* idx = (int64_t*)malloc(sizeof(int64_t) * c->S);
+  double* pr = (double*)malloc(sizeof(double) * c->S);
+  double scale = 1.0 / sqrt((double)c->d);
+  for (int64_t r = lo; r < hi; r++) {
+    int64_t flat = c->rows[r];                 /* (b*Hq + h)*S + i */
+    int64_t i = flat % c->S;
+    for (int t = 0; t < c->d; t++) q[t] = load_elem(c->q, c->dtype, flat * c->d + t);
+    if (c->apply_rope) apex_oracle_rope_row(q, q, c->d, c->m0 + i, c->base);
+    int64_t n = 0;
+    for (int64_t j = 0; j < c->S; j++) {
+      if (!apex_oracle_visible(i, j, c->causal, c->W)) continue;
+      keys[n] = c->krot + j * c->d;
+      vals[n] = c->vd + j * c->d;
+      idx[n] = j;
+      n++;
+    }
+    double* o = c->out + c->row_slot[r] * c->d;
+    attend(q, keys, vals, n, c->d, scale, scores, o, c->probs ? pr : NULL);
+    if (c->probs) {
+      double* prow = c->probs + c->row_slot[r] * c->S;
+      for (int64_t j = 0; j < c->S; j++) prow[j] = 0.0;
+      for (int64_t t = 0; t < n; t++) prow[idx[t]] = pr[t];
+    }
+  }
+  free(q); free(scores); free(keys); free(vals); free(idx); free(pr);
+}
+
+/* Attention output rows of a prefill. q [B,Hq,S,d], k and v [B,Hkv,S,d]
+ * (row-major, fp32 or bf16 bits). rows: flat indices (b*Hq+h)*S+i of the rows
+ * to compute, or NULL for all rows in order. out: [nrows, d] doubles.
+ * probs: optional [nrows, S] softmax weights (0 for masked keys).
+ * Returns 0, or -1 on invalid arguments. */
+int apex_oracle_prefill(const void* q, const void* k, const void* v, int dtype,
+                        int B, int S, int Hq, int Hkv, int d, int causal, int W,
+                        int64_t m0, double base, int apply_rope,
+                        int64_t nrows, const int64_t* rows, double* out, double* probs,
+                        int nthreads) {
+  if (!q || !k || !v || !out || B < 1 || S < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv ||
+      d < 2 || (d & 1) || W < 0 || (W > 0 && !causal) || (dtype != 0 && dtype != 1) ||
+      (apply_rope && !(base > 0.0)))
+    return -1;
+  int64_t total = (int64_t)B * Hq * S;
+  if (!rows) nrows = total;
+  int G = Hq / Hkv;
+  int64_t* all = (int64_t*)malloc(sizeof(int64_t) * (nrows > 0 ? nrows : 1));
+  int64_t* slot = (int64_t*)malloc(sizeof(int64_t) * (nrows > 0 ? nrows : 1));
+  double* krot = (double*)malloc(sizeof(double) * (size_t)S * d);
+  double* vd = (double*)malloc(sizeof(double) * (size_t)S * d);
+  for (int64_t r = 0; r < nrows; r++) {
+    int64_t f = rows ? rows[r] : r;
+    if (f < 0 || f >= total) { free(all); free(slot); free(krot); free(vd); return -1; }
+  }
+  for (int b = 0; b < B; b++) {
+    for (int kvh = 0; kvh < Hkv; kvh++) {
+      int64_t n = 0;
+      for (int64_t r = 0; r < nrows; r++) {
+        int64_t f = rows ? rows[r] : r;
+        int64_t bh = f / S;
+        if (bh / Hq == b && (bh % Hq) / G == kvh) { all[n] = f; slot[n] = r; n++; }
+      }
+      if (n == 0) continue;
+      prefill_ctx c = {q, k, v, dtype, S, Hq, Hkv, d, causal, W, apply_rope, m0, base,
+                       b, kvh, krot, vd, all, slot, out, probs};
+      parallel_for(S, nthreads, prefill_prepare_keys, &c);
+      parallel_for(n, nthreads, prefill_rows, &c);
+    }
+  }
+  free(all); free(slot); free(krot); free(vd);
+  return 0;
+}
+
+/* ----------------------------- decode ----------------------------- */
+typedef struct {
+  const void *q, *kc, *vc, *kn, *vn;
+  int dtype, Sk, Hq, Hkv, d, W, apply_rope;
+  int64_t m;
+  double base;
+  const int64_t* rows;  /* flat b*Hq + h */
+  double* out;
+} decode_ctx;
+
+static void decode_rows(void* p, int64_t lo, int64_t hi) {
+  decode_ctx* c = (decode_ctx*)p;
+  int d = c->d, G = c->Hq / c->Hkv;
+  int64_t n_max = c->m + 1;
+  double* q = (double*)malloc(sizeof(double) * d);
+  double* kd = (double*)malloc(sizeof(double) * (size_t)n_max * d);
+  double* vd = (double*)malloc(sizeof(double) * (size_t)n_max * d);
+  double* scores = (double*)malloc(sizeof(double) * n_max);
+  const double** keys = (const double**)malloc(sizeof(double*) * n_max);
+  const double** vals = (const double**)malloc(sizeof(double*) * n_max);
+  double scale = 1.0 / sqrt((double)d);
+  for (int64_t r = lo; r < hi; r++) {
+    int64_t bh = c->rows ? c->rows[r] : r;
+    int64_t b = bh / c->Hq, h = bh % c->Hq, kvh = h / G;
+    for (int t = 0; t < d; t++) q[t] = load_elem(c->q, c->dtype, bh * d + t);
+    if (c->apply_rope) apex_oracle_rope_row(q, q, d, c->m, c->base);
+    int64_t kv_row0 = (b * c->Hkv + kvh) * (int64_t)c->Sk;
+    int64_t n = 0;
+    for (int64_t j = 0; j <= c->m; j++) {
+      if (!apex_oracle_visible(c->m, j, 1, c->W)) continue;
+      double* kr = kd + n * d;
+      double* vr = vd + n * d;
+      if (j == c->m && c->kn) {
+        for (int t = 0; t < d; t++) kr[t] = load_elem(c->kn, c->dtype, (b * c->Hkv + kvh) * d + t);
+        if (c->apply_rope) apex_oracle_rope_row(kr, kr, d, c->m, c->base);
+      } else {
+        for (int t = 0; t < d; t++) kr[t] = load_elem(c->kc, c->dtype, (kv_row0 + j) * d + t);
+      }
+      if (j == c->m && c->vn) {
+        for (int t = 0; t < d; t++) vr[t] = load_elem(c->vn, c->dtype, (b * c->Hkv + kvh) * d + t);
+      } else {
+        for (int t = 0; t < d; t++) vr[t] = load_elem(c->vc, c->dtype, (kv_row0 + j) * d + t);
+      }
+      keys[n] = kr;
+      vals[n] = vr;
+      n++;
+    }
+    attend(q, keys, vals, n, d, scale, scores, c->out + r * d, NULL);
+  }
+  free(q); free(kd); free(vd); free(scores); free(keys); free(vals);
+}
+
+/* Decode step: one query per (b, h) at position m against a cache of Sk slots.
+ * q [B,Hq,1,d]; k_cache, v_cache [B,Hkv,Sk,d] (slots stored rotated);
+ * k_new, v_new [B,Hkv,1,d] or NULL (then slot m is read from the cache).
+ * rows: flat b*Hq+h, or NULL for all. out [nrows, d]. */
+int apex_oracle_decode(const void* q, const void* k_cache, const void* v_cache,
+                       const void* k_new, const void* v_new, int dtype,
+                       int B, int Sk, int Hq, int Hkv, int d, int W, int64_t m,
+                       double base, int apply_rope,
+                       int64_t nrows, const int64_t* rows, double* out, int nthreads) {
+  if (!q || !k_cache || !v_cache || !out || B < 1 || Sk < 1 || Hq < 1 || Hkv < 1 ||
+      Hq % Hkv || d < 2 || (d & 1) || W < 0 || m < 0 || m >= Sk ||
+      (dtype != 0 && dtype != 1) || (apply_rope && !(base > 0.0)))
+    return -1;
+  int64_t total = (int64_t)B * Hq;
+  if (!rows) nrows = total;
+  for (int64_t r = 0; r < nrows; r++) {
+    int64_t f = rows ? rows[r] : r;
+    if (f < 0 || f >= total) return -1;
+  }
+  decode_ctx c = {q, k_cache, v_cache, k_new, v_new, dtype, Sk, Hq, Hkv, d, W, apply_rope,
+                  m, base, rows, out};
+  parallel_for(nrows, nthreads, decode_rows, &c);
+  return 0;
+}
