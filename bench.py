@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark of the RoPE + attention hot path on one MI355X.
+
+One step = one pass of the path over one batch of the GQA causal prefill
+workload (B=4, S=2048, H_q=32, H_kv=8, d_h=128, bf16, RoPE base 10000):
+  1. RoPE of K into the rotated-key buffer (apex_rope_qk, elementwise launch);
+  2. attention with RoPE of Q fused into its tile loads (apex_attn_prefill,
+     apply_rope=2).
+Throughput is mask-adjusted: 4 * B * H_q * d_h FLOPs per visible (query, key)
+pair (RoPE and softmax are not credited). Inputs are seeded N(0,1) draws
+already resident in HBM when the timed region starts.
+
+The line also carries the split-K decode workload (B=64, Sk=32768, H_q=128,
+H_kv=8) in HBM GB/s, the window / long-context prefill workloads, the
+roofline of the dominant kernel, and the fp64 CPU oracle timed on a bounded
+sample of the same workload (a baseline, not a target).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+HEADLINE = "gqa_prefill_s2048"
+DECODE = "gqa_decode_sk32768"
+OTHERS = ("window_prefill_s16384_w4096", "local_prefill_s65536_w512")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_gqa_s2048_traffic.json")
+PREFILL_SOURCES = ("transformer_attention_amd/csrc/prefill_kernel.hpp",
+                   "transformer_attention_amd/csrc/device_common.hpp")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def n_visible(S, causal, W):
+    """Visible (query, key) pairs of one (b, h): key j visible to query i iff
+    j <= i and, with a window, i - j < W (Part 2, §10.2)."""
+    if not causal:
+        return S * S
+    if W == 0 or W >= S:
+        return S * (S + 1) // 2
+    # rows i < W see i + 1 keys, the rest see W keys
+    return W * (W + 1) // 2 + (S - W) * W
+
+
+def prefill_flops(w):
+    return 4 * w["B"] * w["Hq"] * w["d"] * n_visible(w["S"], w["causal"], w["W"])
+
+
+def prefill_bytes(w):
+    """Algorithmic HBM bytes of the attention launch: q, k, v read once, o written once."""
+    e = 2 if w["dtype"] == "bf16" else 4
+    return e * w["d"] * w["S"] * w["B"] * (2 * w["Hq"] + 2 * w["Hkv"])
+
+
+def decode_bytes(w):
+    """Algorithmic bytes of one decode call: the K and V caches read once, q
+    read, o written, the new key and value read."""
+    B, Sk, Hq, Hkv, d = w["B"], w["Sk"], w["Hq"], w["Hkv"], w["d"]
+    return 2 * (2 * B * Hkv * Sk * d + 2 * B * Hq * d + 2 * B * Hkv * d)
+
+
+def sources_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch of the prefill kernel from the committed rocprofv3
+    counter summary, or None when the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != sources_sha(PREFILL_SOURCES):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def time_prefill(taa, torch, name, steps, warmup):
+    import apex_inputs
+    w = apex_inputs.WORKLOADS[name]
+    q, k, v = apex_inputs.workload_inputs(name, device="cuda")
+    kr, o = torch.empty_like(k), torch.empty_like(q)
+    kw = dict(causal=w["causal"], W=w["W"], m0=w["m0"], base=w["base"])
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        taa.apex_rope_qk(None, k, k_out=kr, m0=w["m0"], base=w["base"])
+        if ev:
+            ev[1].record()
+        taa.apex_attn_prefill(q, kr, v, o, None, apply_rope=2, **kw)
+        if ev:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    rope_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    attn_min = min(e[1].elapsed_time(e[2]) for e in evs)
+    del q, k, v, kr, o
+    return w, wall * 1e3, rope_ms, attn_ms, attn_min
+
+
+def time_decode(taa, torch, steps, warmup):
+    import apex_inputs
+    w = apex_inputs.WORKLOADS[DECODE]
+    q, kc, vc, kn, vn = apex_inputs.workload_inputs(DECODE, device="cuda")
+    B, Hq, _, d = q.shape
+    Hkv, Sk = kc.shape[1], kc.shape[2]
+    o = torch.empty_like(q)
+    ws = torch.empty(taa.apex_attn_decode_workspace_bytes(B, Hq, Hkv, Sk, d), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        taa.apex_attn_decode(q, kc, vc, kn, vn, o, m=w["m"], W=w["W"], base=w["base"],
+                             workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    del q, kc, vc, kn, vn, o, ws
+    return w, sum(ms) / len(ms), ms[len(ms) // 2], ms[0]
+
+
+def cpu_baseline(w, budget_s):
+    """Time the fp64 oracle on whole query heads of the workload (all rows of
+    each), as many as fit in about budget_s seconds."""
+    import apex_inputs
+    import oracle
+    threads = oracle.default_threads()
+    B, S, Hq, Hkv, d = w["B"], w["S"], w["Hq"], w["Hkv"], w["d"]
+    # batch element 0 of the workload's shape, drawn on the host
+    q, k, v = apex_inputs.prefill_inputs(1, S, Hq, Hkv, d, w["dtype"], seed=w["seed"],
+                                         device="cpu")
+    per_head = 4 * d * n_visible(S, w["causal"], w["W"])
+    kw = dict(causal=w["causal"], W=w["W"], m0=w["m0"], base=w["base"], nthreads=threads)
+
+    def run(n_heads):
+        rows = [h * S + i for h in range(n_heads) for i in range(S)]
+        t0 = time.perf_counter()
+        oracle.prefill(q, k, v, rows=rows, **kw)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    n = max(1, min(Hq, int(budget_s / max(t1, 1e-6))))
+    t = run(n) if n > 1 else t1
+    return {"value": round(n * per_head / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d query head(s) x all %d rows of %s (one batch element drawn on "
+                      "the host), %.1f s, "
+                      "%.3g GFLOP mask-adjusted" % (n, S, HEADLINE, t, n * per_head / 1e9)}
+
+
+def copy_calibration(torch):
+    """A plain elementwise copy of known size (read 1 GiB, write 1 GiB), run for
+    scaling the rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_kernel": "neg", "read_bytes": 4 * n, "write_bytes": 4 * n,
+                      "launches": 5}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline prefill (for profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run the counter-calibration copy kernel and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    from transformer_attention_amd import build as hipbuild
+    if not os.path.exists(hipbuild.LIB):
+        hipbuild.build()
+    import transformer_attention_amd as taa
+    taa.lib()
+
+    log("timing %s: %d warmup + %d steps" % (HEADLINE, args.warmup, args.steps))
+    w, ms_step, rope_ms, attn_ms, attn_min = time_prefill(taa, torch, HEADLINE, args.steps,
+                                                         args.warmup)
+    flops = prefill_flops(w)
+    value = flops / (ms_step * 1e-3) / 1e12
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    log("step %.4f ms (rope_k %.4f ms, attention %.4f ms) -> %.1f TFLOP/s"
+        % (ms_step, rope_ms, attn_ms, value))
+
+    extra = {}
+    if not args.headline_only:
+        dsteps = max(5, args.steps)
+        log("timing %s: %d warmup + %d calls" % (DECODE, args.warmup, dsteps))
+        dw, d_mean, d_med, d_min = time_decode(taa, torch, dsteps, args.warmup)
+        dbytes = decode_bytes(dw)
+        gbs = dbytes / (d_mean * 1e-3) / 1e9
+        log("decode %.4f ms -> %.1f GB/s" % (d_mean, gbs))
+        extra["decode"] = {
+            "workload": DECODE, "metric": "decode HBM GB/s (algorithmic bytes)",
+            "value": round(gbs, 1), "unit": "GB/s", "ms_per_call": round(d_mean, 4),
+            "ms_median": round(d_med, 4), "ms_min": round(d_min, 4),
+            "algorithmic_bytes": dbytes, "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "note": "whole call: split-K pass + combine pass, events on the launch stream"}
+        others = {}
+        for name in OTHERS:
+            log("timing %s" % name)
+            ow, oms, orope, oattn, _ = time_prefill(taa, torch, name, max(3, args.steps // 4),
+                                                    2)
+            of = prefill_flops(ow)
+            others[name] = {"ms_per_step": round(oms, 4), "rope_k_ms": round(orope, 4),
+                            "attention_ms": round(oattn, 4),
+                            "tflops": round(of / (oms * 1e-3) / 1e12, 1),
+                            "attention_tflops": round(of / (oattn * 1e-3) / 1e12, 1),
+                            "frac_of_bf16_peak": round(of / (oms * 1e-3) / 1e12
+                                                       / PEAK_BF16_TFLOPS, 4)}
+        extra["other_workloads"] = others
+        torch.cuda.empty_cache()
+
+    line = {
+        "metric": "attention TFLOP/s (mask-adjusted) + % bf16 MFMA peak; decode HBM GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": HEADLINE, "B": w["B"], "S": w["S"], "H_q": w["Hq"],
+                   "H_kv": w["Hkv"], "d_h": w["d"], "causal": w["causal"], "W": w["W"],
+                   "rope_base": w["base"], "mask_adjusted_flops": flops},
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"kernel": "prefill_bf16_kernel<128>", "bound": "mfma",
+                     "achieved": round(attn_tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": load_traffic(), "launch_ms_mean": round(attn_ms, 4),
+                     "launch_ms_min": round(attn_min, 4),
+                     "algorithmic_bytes": prefill_bytes(w)},
+        "rope_k_ms": round(rope_ms, 4),
+    }
+    line.update(extra)
+    if args.cpu_budget > 0:
+        log("timing the CPU oracle (budget %.0f s)" % args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -51,17 +51,23 @@ typedef enum {
 enum { APEX_F32 = 0, APEX_BF16 = 1 };
 
 /*
- * apex_rope_qk -- rotate Q and K in place (Part 1, §4.2-§4.4).
- *   q: [B, H_q, S, d_h], rotated in place; row s sits at position m0 + s.
- *   k: [B, H_kv, S, d_h], rotated in place at the same positions, or NULL.
+ * apex_rope_qk -- rotate Q and/or K (Part 1, §4.2-§4.4).
+ *   q: [B, H_q, S, d_h] read; q_out: [B, H_q, S, d_h] receives RoPE(q).
+ *   k: [B, H_kv, S, d_h] read; k_out: [B, H_kv, S, d_h] receives RoPE(k).
+ *   Row s of every head sits at position m0 + s. Each pair (q, q_out) and
+ *   (k, k_out) is either both NULL or both given, at least one pair is given,
+ *   and an output may equal its own input (in-place rotation) but must not
+ *   overlap any other buffer.
  *   base: the RoPE base b (> 0), 10000 on the pages.
  * Angles are formed in fp64 and reduced to one turn before the fp32 sine and
- * cosine, so positions up to 2^31 keep full fp32 accuracy.
- * Errors: APEX_EINVAL for B, S, H_q < 1, H_kv < 1 when k is given, m0 < 0,
- * base <= 0, q == NULL, or an unknown dtype.
+ * cosine, so large positions keep full fp32 accuracy.
+ * Errors: APEX_EINVAL for B or S < 1, H_q < 1 when q is given, H_kv < 1 when
+ * k is given, a half-given pair, no pair, m0 < 0, base <= 0, an unknown
+ * dtype; APEX_EUNSUPPORTED for d_h not 64 or 128.
  */
-int apex_rope_qk(void* q, void* k, int B, int S, int H_q, int H_kv, int d_h,
-                 int64_t m0, double base, int dtype, void* stream);
+int apex_rope_qk(const void* q, const void* k, void* q_out, void* k_out, int B, int S,
+                 int H_q, int H_kv, int d_h, int64_t m0, double base, int dtype,
+                 void* stream);
 
 /*
  * apex_attn_prefill -- o = softmax(RoPE(q) RoPE(k)^T / sqrt(d_h)) v with GQA
@@ -73,15 +79,21 @@ int apex_rope_qk(void* q, void* k, int B, int S, int H_q, int H_kv, int d_h,
  *   causal: 1 = key j visible to query i only if j <= i; 0 = all visible.
  *   W: window width (> 0 requires causal = 1); 0 = no window.
  *   m0: position of row 0 (>= 0). The mask depends on i - j only.
- *   apply_rope: 1 = q and k are raw: q is rotated while its tiles load and k
- *     is rotated once into k_rope_out, which the attention then reads;
- *     0 = q and k already hold rotated values, k_rope_out is ignored.
+ *   apply_rope:
+ *     1 = q and k are raw: k is rotated once into k_rope_out (one elementwise
+ *         launch), then the attention launch rotates q while its tiles load
+ *         and reads the rotated keys from k_rope_out;
+ *     2 = q is raw and k already holds rotated keys (for example a cache
+ *         filled by an earlier call): only the attention launch runs, rotating
+ *         q as it loads; k_rope_out is ignored;
+ *     0 = q and k both hold rotated values; k_rope_out is ignored.
  *   k_rope_out: [B, H_kv, S, d_h] receives RoPE(k) when apply_rope = 1 (the
  *     values a KV cache stores). It may equal k (in-place rotation) but must
  *     not overlap q, v or o.
  * Errors: APEX_EINVAL for H_q % H_kv != 0, sizes < 1, W < 0, W > 0 with
- * causal = 0, m0 < 0, base <= 0 with apply_rope, a NULL required pointer, an
- * unknown dtype; APEX_EUNSUPPORTED for d_h not 64 or 128.
+ * causal = 0, m0 < 0, apply_rope not 0/1/2, base <= 0 with apply_rope, a
+ * NULL required pointer, an unknown dtype; APEX_EUNSUPPORTED for d_h not 64
+ * or 128.
  */
 int apex_attn_prefill(const void* q, const void* k, const void* v, void* o,
                       void* k_rope_out, int B, int S, int H_q, int H_kv, int d_h,

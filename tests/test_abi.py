@@ -1,0 +1,153 @@
+"""The C ABI library loads, exports every symbol include/apex_attn.h declares,
+and rejects every invalid argument with the documented status before touching
+the GPU (these calls return before any HIP call, so they run on the CPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "apex_attn.h")
+
+EINVAL, EUNSUP, EWS = -1, -2, -3
+P = 0x10000  # a non-null pointer value; never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def L():
+    import transformer_attention_amd as taa
+    if not os.path.exists(taa.lib_path()):
+        from transformer_attention_amd import build
+        build.build()
+    return taa.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(apex_\w+)\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["apex_attn_decode", "apex_attn_decode_workspace_bytes",
+                                    "apex_attn_prefill", "apex_rope_qk", "apex_strerror"]
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert isinstance(getattr(L, name), ctypes._CFuncPtr)
+
+
+def test_strerror_covers_every_status(L):
+    for s in (0, -1, -2, -3, -4, 7):
+        assert L.apex_strerror(s)
+    assert L.apex_strerror(-3).decode().startswith("decode workspace")
+
+
+def _rope(L, q=P, k=P, qo=P, ko=P, B=1, S=8, Hq=2, Hkv=1, d=64, m0=0, base=1e4, dtype=1):
+    return L.apex_rope_qk(q, k, qo, ko, B, S, Hq, Hkv, d, m0, base, dtype, None)
+
+
+def test_rope_rejects(L):
+    assert _rope(L, q=None) == EINVAL           # q given without q_out and vice versa
+    assert _rope(L, qo=None) == EINVAL
+    assert _rope(L, k=None) == EINVAL
+    assert _rope(L, ko=None) == EINVAL
+    assert _rope(L, q=None, qo=None, k=None, ko=None) == EINVAL
+    assert _rope(L, B=0) == EINVAL
+    assert _rope(L, S=0) == EINVAL
+    assert _rope(L, Hq=0) == EINVAL
+    assert _rope(L, Hkv=0) == EINVAL
+    assert _rope(L, m0=-1) == EINVAL
+    assert _rope(L, base=0.0) == EINVAL
+    assert _rope(L, base=-5.0) == EINVAL
+    assert _rope(L, dtype=7) == EINVAL
+    assert _rope(L, d=63) == EINVAL
+    assert _rope(L, d=96) == EUNSUP
+    assert _rope(L, d=256) == EUNSUP
+    # an absent pair does not need its head count
+    assert _rope(L, k=None, ko=None, Hkv=0, d=96) == EUNSUP
+    assert _rope(L, q=None, qo=None, Hq=0, d=96) == EUNSUP
+
+
+def _prefill(L, q=P, k=P, v=P, o=P, kr=P, B=1, S=8, Hq=4, Hkv=2, d=128, causal=1, W=0, m0=0,
+             base=1e4, rope=1, dtype=1):
+    return L.apex_attn_prefill(q, k, v, o, kr, B, S, Hq, Hkv, d, causal, W, m0, base, rope, dtype,
+                               None)
+
+
+def test_prefill_rejects(L):
+    for kw in (dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(kr=None)):
+        assert _prefill(L, **kw) == EINVAL, kw
+    assert _prefill(L, Hq=3, Hkv=2) == EINVAL      # H_q % H_kv != 0
+    assert _prefill(L, B=0) == EINVAL
+    assert _prefill(L, S=0) == EINVAL
+    assert _prefill(L, Hkv=0) == EINVAL
+    assert _prefill(L, W=-1) == EINVAL
+    assert _prefill(L, causal=0, W=4) == EINVAL     # a window needs the causal mask
+    assert _prefill(L, causal=2) == EINVAL
+    assert _prefill(L, m0=-3) == EINVAL
+    assert _prefill(L, base=0.0) == EINVAL
+    assert _prefill(L, rope=3) == EINVAL
+    assert _prefill(L, rope=-1) == EINVAL
+    assert _prefill(L, dtype=2) == EINVAL
+    assert _prefill(L, d=7) == EINVAL
+    assert _prefill(L, d=32) == EUNSUP
+    assert _prefill(L, d=80) == EUNSUP
+
+
+def test_prefill_rope_modes_and_rope_buffer(L):
+    # k_rope_out is needed only when apply_rope = 1; other checks still apply.
+    assert _prefill(L, kr=None, rope=0, Hq=3, Hkv=2) == EINVAL
+    assert _prefill(L, kr=None, rope=0, base=0.0, d=96) == EUNSUP  # base unused without RoPE
+    assert _prefill(L, kr=None, rope=2, d=96) == EUNSUP            # q-only RoPE: no buffer
+    assert _prefill(L, kr=None, rope=2, base=0.0) == EINVAL
+
+
+def test_decode_workspace_bytes(L):
+    f = L.apex_attn_decode_workspace_bytes
+    assert f(0, 8, 8, 16, 64) == 0
+    assert f(1, 3, 2, 16, 64) == 0
+    assert f(1, 8, 8, 0, 64) == 0
+    n = f(64, 128, 8, 32768, 128)
+    # partial results: per (b, h, part) d_h + 2 fp32; parts are whole waves of 4
+    assert n > 0 and n % (64 * 128 * 130 * 4) == 0 and (n // (64 * 128 * 130 * 4)) % 4 == 0
+    assert f(1, 8, 8, 16, 64) > 0
+
+
+def _decode(L, q=P, kc=P, vc=P, kn=P, vn=P, o=P, B=2, Sk=64, Hq=16, Hkv=1, d=128, W=0, m=63,
+            base=1e4, rope=1, ws=P, wsb=None, dtype=1):
+    if wsb is None:
+        wsb = L.apex_attn_decode_workspace_bytes(B, Hq, Hkv, Sk, d) if Hkv > 0 else 0
+    return L.apex_attn_decode(q, kc, vc, kn, vn, o, B, Sk, Hq, Hkv, d, W, m, base, rope, ws, wsb,
+                              dtype, None)
+
+
+def test_decode_rejects(L):
+    for kw in (dict(q=None), dict(kc=None), dict(vc=None), dict(o=None)):
+        assert _decode(L, **kw) == EINVAL, kw
+    assert _decode(L, kn=None) == EINVAL   # exactly one of k_new / v_new
+    assert _decode(L, vn=None) == EINVAL
+    assert _decode(L, Hq=12, Hkv=8) == EINVAL
+    assert _decode(L, B=0) == EINVAL
+    assert _decode(L, Sk=0, wsb=1 << 20) == EINVAL
+    assert _decode(L, W=-2) == EINVAL
+    assert _decode(L, m=-1) == EINVAL
+    assert _decode(L, m=64) == EINVAL       # m >= Sk
+    assert _decode(L, base=-1.0) == EINVAL
+    assert _decode(L, rope=3) == EINVAL
+    assert _decode(L, dtype=5) == EINVAL
+    assert _decode(L, d=9) == EINVAL
+    assert _decode(L, d=96) == EUNSUP
+    assert _decode(L, dtype=0) == EUNSUP    # decode is built for bf16 caches
+    assert _decode(L, ws=None) == EWS
+    assert _decode(L, wsb=16) == EWS
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import transformer_attention_amd as taa
+    q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        taa.apex_rope_qk(q, None)

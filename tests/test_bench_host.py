@@ -1,0 +1,34 @@
+"""Host-side arithmetic of bench.py: visible-pair counts and algorithmic bytes."""
+import subprocess
+import sys
+
+import pytest
+
+import bench
+import oracle
+
+
+@pytest.mark.parametrize("S", [1, 2, 7, 64, 100])
+@pytest.mark.parametrize("W", [0, 1, 3, 64, 99, 100, 1000])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_n_visible_matches_the_mask(S, W, causal):
+    if W and not causal:
+        return
+    brute = sum(oracle.visible(i, j, causal, W) for i in range(S) for j in range(S))
+    assert bench.n_visible(S, causal, W) == brute
+
+
+def test_workload_counts():
+    import apex_inputs
+    w = apex_inputs.WORKLOADS
+    assert bench.n_visible(2048, 1, 0) == 2098176
+    assert bench.n_visible(16384, 1, 4096) == 58722304
+    assert bench.n_visible(65536, 1, 512) == 33423616
+    assert bench.prefill_flops(w["gqa_prefill_s2048"]) == 137506062336
+    assert bench.decode_bytes(w["gqa_decode_sk32768"]) == 8594391040
+
+
+def test_multi_gpu_request_is_refused():
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                       text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr

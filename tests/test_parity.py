@@ -1,0 +1,288 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Inputs are seeded N(0,1) draws (apex_inputs) made on the GPU; the oracle gets
+exact CPU copies of the same inputs. Bars (per element):
+  fp32 workloads: max |gpu - oracle| <= 1e-4
+  bf16 workloads: max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3
+Small shapes are compared on every output element; the full-size workloads,
+run in the same launch configuration the benchmark times, are compared on
+sampled rows (tile edges, first/last rows and heads, random rows).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import apex_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": dict(max_abs=1e-4, mean_abs=1e-4), "bf16": dict(max_abs=2e-2, mean_abs=2e-3)}
+
+
+def _say(*a):
+    print("[parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def taa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import transformer_attention_amd as t
+    t.lib()  # raises if the HIP library is not built
+    return t
+
+
+def _check(got, ref, dtype, what):
+    got = got.detach().to("cpu", torch.float64).numpy().reshape(ref.shape)
+    err = np.abs(got - ref)
+    mx, mean = float(err.max()), float(err.mean())
+    _say("%s: max_abs %.3g mean_abs %.3g (%d values)" % (what, mx, mean, err.size))
+    assert np.all(np.isfinite(got)), what
+    assert mx <= TOL[dtype]["max_abs"], (what, mx)
+    assert mean <= TOL[dtype]["mean_abs"], (what, mean)
+    return mx, mean
+
+
+def _rows(B, Hq, S, n_random, seed):
+    rng = np.random.default_rng(seed)
+    iset = [i for i in (0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 255, 256, 511, 512, 513,
+                        S // 2, S - 65, S - 64, S - 33, S - 32, S - 2, S - 1) if 0 <= i < S]
+    rows = set()
+    for b in sorted({0, B - 1}):
+        for h in sorted({0, Hq - 1, int(rng.integers(Hq))}):
+            for i in iset:
+                rows.add((b * Hq + h) * S + i)
+    rows.update(int(x) for x in rng.integers(0, B * Hq * S, size=n_random))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+# ---------------------------------------------------------------- RoPE ----
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("m0", [0, 1000, 65535 - 40, 10 ** 6])
+def test_rope_matches_oracle(taa, dtype, d, m0):
+    _say("rope", dtype, d, m0)
+    q, k, _ = apex_inputs.prefill_inputs(2, 41, 3, 2, d, dtype, seed=11, device="cuda")
+    q0, k0 = q.cpu(), k.cpu()
+    taa.apex_rope_qk(q, k, m0=m0)
+    torch.cuda.synchronize()
+    for got, src in ((q, q0), (k, k0)):
+        x = src.double().numpy()
+        ref = np.empty_like(x)
+        for b in range(x.shape[0]):
+            for h in range(x.shape[1]):
+                for s in range(x.shape[2]):
+                    ref[b, h, s] = oracle.rope_row(x[b, h, s], m0 + s)
+        g = got.cpu().double().numpy()
+        if dtype == "f32":
+            assert np.max(np.abs(g - ref)) <= 1e-5
+        else:  # one bf16 rounding of the rotated value
+            assert np.all(np.abs(g - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6)
+
+
+# -------------------------------------------------------------- prefill ----
+PREFILL_CASES = [
+    # B, S, Hq, Hkv, d, causal, W, m0, dtype, apply_rope
+    (1, 1, 2, 1, 128, 1, 0, 0, "bf16", 1),
+    (1, 2, 4, 2, 64, 1, 0, 0, "bf16", 1),
+    (2, 3, 4, 4, 128, 1, 0, 7, "bf16", 1),
+    (1, 17, 8, 2, 128, 1, 5, 0, "bf16", 1),
+    (1, 64, 16, 1, 128, 1, 0, 1000, "bf16", 1),
+    (2, 65, 8, 1, 64, 1, 2, 0, "bf16", 1),
+    (1, 129, 4, 4, 128, 0, 0, 0, "bf16", 1),
+    (1, 300, 32, 8, 128, 1, 64, 1000, "bf16", 1),
+    (1, 513, 8, 8, 64, 1, 1, 0, "bf16", 1),
+    (1, 1000, 12, 4, 128, 1, 0, 0, "bf16", 1),
+    (1, 777, 6, 1, 128, 0, 0, 0, "bf16", 1),
+    (2, 700, 32, 8, 128, 1, 0, 0, "bf16", 0),
+    (1, 640, 64, 8, 128, 1, 128, 0, "bf16", 1),
+    (1, 128, 4, 2, 64, 1, 0, 0, "f32", 1),
+    (1, 77, 4, 1, 128, 1, 9, 5, "f32", 1),
+    (2, 33, 2, 2, 64, 0, 0, 0, "f32", 1),
+    (1, 300, 8, 2, 128, 1, 0, 0, "f32", 0),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_small(taa, case):
+    B, S, Hq, Hkv, d, causal, W, m0, dtype, rope = case
+    _say("prefill", case)
+    q, k, v = apex_inputs.prefill_inputs(B, S, Hq, Hkv, d, dtype, seed=S + Hq, device="cuda")
+    o = torch.empty_like(q)
+    kr = torch.empty_like(k)
+    taa.apex_attn_prefill(q, k, v, o, kr, causal=causal, W=W, m0=m0, apply_rope=rope)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), causal=causal, W=W, m0=m0, apply_rope=rope)
+    _check(o, ref, dtype, "prefill %s" % (case,))
+
+
+def test_k_rope_out_holds_rotated_keys_and_may_alias_k(taa):
+    B, S, Hq, Hkv, d = 1, 200, 8, 2, 128
+    q, k, v = apex_inputs.prefill_inputs(B, S, Hq, Hkv, d, "bf16", seed=5, device="cuda")
+    o1, kr = torch.empty_like(q), torch.empty_like(k)
+    taa.apex_attn_prefill(q, k, v, o1, kr, W=50, m0=3)
+    k2 = k.clone()
+    taa.apex_rope_qk(k2, None, m0=3)  # rotates its first argument only
+    torch.cuda.synchronize()
+    assert torch.equal(kr, k2)  # same kernel, same bits
+    o2 = torch.empty_like(q)
+    k3 = k.clone()
+    taa.apex_attn_prefill(q, k3, v, o2, k3, W=50, m0=3)  # rotate in place
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(k3, kr)
+
+
+def test_fused_rope_agrees_with_prerotated_inputs(taa):
+    B, S, Hq, Hkv, d = 1, 333, 16, 4, 128
+    q, k, v = apex_inputs.prefill_inputs(B, S, Hq, Hkv, d, "bf16", seed=6, device="cuda")
+    o_fused, kr = torch.empty_like(q), torch.empty_like(k)
+    taa.apex_attn_prefill(q, k, v, o_fused, kr, m0=40000)
+    qr, kr2 = q.clone(), k.clone()
+    taa.apex_rope_qk(qr, kr2, m0=40000)
+    o_pre = torch.empty_like(q)
+    taa.apex_attn_prefill(qr, kr2, v, o_pre, None, m0=40000, apply_rope=0)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), m0=40000)
+    _check(o_fused, ref, "bf16", "fused RoPE")
+    _check(o_pre, ref, "bf16", "pre-rotated")
+
+
+# ------------------------------------------------------ full workloads ----
+def _run_prefill_workload(taa, name, n_random):
+    w = apex_inputs.WORKLOADS[name]
+    _say("workload", name, w)
+    q, k, v = apex_inputs.workload_inputs(name, device="cuda")
+    o, kr = torch.empty_like(q), torch.empty_like(k)
+    taa.apex_attn_prefill(q, k, v, o, kr, causal=w["causal"], W=w["W"], m0=w["m0"],
+                          base=w["base"], apply_rope=1)
+    torch.cuda.synchronize()
+    B, Hq, S, d = q.shape
+    if n_random is None:
+        ref = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), causal=w["causal"], W=w["W"],
+                             m0=w["m0"], base=w["base"])
+        return _check(o, ref, w["dtype"], name)
+    rows = _rows(B, Hq, S, n_random, seed=w["seed"])
+    ref = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), causal=w["causal"], W=w["W"], m0=w["m0"],
+                         base=w["base"], rows=rows)
+    got = o.reshape(-1, d)[torch.from_numpy(rows).to(o.device)]
+    return _check(got, ref, w["dtype"], "%s (%d sampled rows)" % (name, rows.size))
+
+
+def test_workload_tiny_prefill_f32(taa):
+    _run_prefill_workload(taa, "tiny_prefill_f32", None)
+
+
+def test_workload_gqa_prefill_s2048(taa):
+    _run_prefill_workload(taa, "gqa_prefill_s2048", 3000)
+
+
+def test_workload_window_prefill_s16384_w4096(taa):
+    _run_prefill_workload(taa, "window_prefill_s16384_w4096", 1500)
+
+
+def test_workload_local_prefill_s65536_w512(taa):
+    _run_prefill_workload(taa, "local_prefill_s65536_w512", 3000)
+
+
+# --------------------------------------------------------------- decode ----
+DECODE_CASES = [
+    # B, Sk, Hq, Hkv, d, W, m, with_new, apply_rope
+    (1, 1, 16, 1, 128, 0, 0, True, 1),
+    (2, 5, 4, 1, 128, 0, 4, True, 1),
+    (1, 33, 16, 1, 64, 0, 20, True, 1),
+    (2, 100, 32, 2, 128, 7, 99, True, 1),
+    (1, 1000, 8, 8, 128, 64, 999, False, 0),
+    (1, 5000, 64, 2, 128, 0, 4321, True, 1),
+    (3, 4096, 12, 4, 64, 100, 4095, True, 1),
+    (2, 20000, 16, 1, 128, 0, 19999, True, 1),
+]
+
+
+def _decode_inputs(B, Sk, Hq, Hkv, d, seed):
+    return apex_inputs.decode_inputs(B, Sk, Hq, Hkv, d, "bf16", seed=seed, device="cuda")
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_decode_small(taa, case):
+    B, Sk, Hq, Hkv, d, W, m, with_new, rope = case
+    _say("decode", case)
+    q, kc, vc, kn, vn = _decode_inputs(B, Sk, Hq, Hkv, d, seed=Sk + Hq)
+    if not with_new:
+        kn = vn = None
+    kc0, vc0 = kc.cpu(), vc.cpu()
+    o = torch.empty_like(q)
+    ws = torch.empty(taa.apex_attn_decode_workspace_bytes(B, Hq, Hkv, Sk, d), dtype=torch.uint8,
+                     device="cuda")
+    taa.apex_attn_decode(q, kc, vc, kn, vn, o, m=m, W=W, apply_rope=rope, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.decode(q.cpu(), kc0, vc0, kn.cpu() if with_new else None,
+                        vn.cpu() if with_new else None, m=m, W=W, apply_rope=rope)
+    _check(o, ref, "bf16", "decode %s" % (case,))
+    kc1, vc1 = kc.cpu(), vc.cpu()
+    other = torch.ones(Sk, dtype=torch.bool)
+    other[m] = False
+    assert torch.equal(kc1[:, :, other], kc0[:, :, other])  # only slot m may change
+    assert torch.equal(vc1[:, :, other], vc0[:, :, other])
+    if with_new:
+        assert torch.equal(vc1[:, :, m], vn.cpu()[:, :, 0])
+        x = kn.cpu().double().numpy()[:, :, 0]
+        want = np.array([[oracle.rope_row(x[b, h], m) if rope else x[b, h] for h in range(Hkv)]
+                         for b in range(B)])
+        got = kc1[:, :, m].double().numpy()
+        assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -8 + 1e-6)
+
+
+def test_decode_repeat_is_idempotent(taa):
+    B, Sk, Hq, Hkv, d = 2, 3000, 32, 2, 128
+    q, kc, vc, kn, vn = _decode_inputs(B, Sk, Hq, Hkv, d, seed=77)
+    ws = torch.empty(taa.apex_attn_decode_workspace_bytes(B, Hq, Hkv, Sk, d), dtype=torch.uint8,
+                     device="cuda")
+    o1, o2 = torch.empty_like(q), torch.empty_like(q)
+    taa.apex_attn_decode(q, kc, vc, kn, vn, o1, m=Sk - 1, workspace=ws)
+    taa.apex_attn_decode(q, kc, vc, kn, vn, o2, m=Sk - 1, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_decode_equals_last_prefill_row(taa):
+    B, S, Hq, Hkv, d = 1, 1500, 32, 2, 128
+    q, k, v = apex_inputs.prefill_inputs(B, S, Hq, Hkv, d, "bf16", seed=8, device="cuda")
+    o, kr = torch.empty_like(q), torch.empty_like(k)
+    taa.apex_attn_prefill(q, k, v, o, kr)
+    kc, vc = kr.clone(), v.clone()
+    kc[:, :, S - 1].zero_()  # slot m comes from k_new / v_new
+    vc[:, :, S - 1].zero_()
+    od = torch.empty(B, Hq, 1, d, dtype=q.dtype, device=q.device)
+    ws = torch.empty(taa.apex_attn_decode_workspace_bytes(B, Hq, Hkv, S, d), dtype=torch.uint8,
+                     device="cuda")
+    taa.apex_attn_decode(q[:, :, S - 1:].contiguous(), kc, vc, k[:, :, S - 1:].contiguous(),
+                         v[:, :, S - 1:].contiguous(), od, m=S - 1, workspace=ws)
+    torch.cuda.synchronize()
+    diff = (od[:, :, 0].float() - o[:, :, S - 1].float()).abs().max().item()
+    _say("decode vs prefill last row: max_abs %.3g" % diff)
+    assert diff <= 2e-2
+
+
+def test_workload_gqa_decode_sk32768(taa):
+    name = "gqa_decode_sk32768"
+    w = apex_inputs.WORKLOADS[name]
+    _say("workload", name, w)
+    q, kc, vc, kn, vn = apex_inputs.workload_inputs(name, device="cuda")
+    B, Hq, _, d = q.shape
+    Hkv, Sk = kc.shape[1], kc.shape[2]
+    bs = [0, 17, B - 1]
+    saved = [(kc[b].cpu(), vc[b].cpu()) for b in bs]  # inputs as they were before the call
+    o = torch.empty_like(q)
+    ws = torch.empty(taa.apex_attn_decode_workspace_bytes(B, Hq, Hkv, Sk, d), dtype=torch.uint8,
+                     device="cuda")
+    taa.apex_attn_decode(q, kc, vc, kn, vn, o, m=w["m"], W=w["W"], base=w["base"], workspace=ws)
+    torch.cuda.synchronize()
+    for b, (kcb, vcb) in zip(bs, saved):
+        ref = oracle.decode(q[b:b + 1].cpu(), kcb[None], vcb[None], kn[b:b + 1].cpu(),
+                            vn[b:b + 1].cpu(), m=w["m"], W=w["W"], base=w["base"])
+        _check(o[b:b + 1], ref, "bf16", "%s batch %d (all %d heads)" % (name, b, Hq))

@@ -1,0 +1,129 @@
+"""ctypes binding of libapex_attn.so: argument marshalling only.
+
+Each function has the name and the arguments of its C entry point
+(include/apex_attn.h); torch tensors stand in for device pointers and the
+stream defaults to torch's current stream on the tensors' device.
+"""
+import ctypes
+import os
+
+import torch
+
+APEX_F32, APEX_BF16 = 0, 1
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB = os.path.join(_PKG, "libapex_attn.so")
+_lib = None
+
+
+class ApexError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__("%s failed: %s (%d)" % (fn, apex_strerror(status), status))
+        self.status = status
+
+
+def lib_path():
+    return _LIB
+
+
+def lib():
+    """Load the built library; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            raise RuntimeError("libapex_attn.so is not built; run "
+                               "`python -m transformer_attention_amd.build` first")
+        L = ctypes.CDLL(_LIB)
+        i32, i64, dbl, vp, sz = (ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p,
+                                 ctypes.c_size_t)
+        L.apex_rope_qk.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, dbl, i32, vp]
+        L.apex_rope_qk.restype = i32
+        L.apex_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64,
+                                        dbl, i32, i32, vp]
+        L.apex_attn_prefill.restype = i32
+        L.apex_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.apex_attn_decode_workspace_bytes.restype = sz
+        L.apex_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
+                                       dbl, i32, vp, sz, i32, vp]
+        L.apex_attn_decode.restype = i32
+        L.apex_strerror.argtypes = [i32]
+        L.apex_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def apex_strerror(status):
+    return lib().apex_strerror(int(status)).decode()
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return APEX_BF16
+    if t.dtype == torch.float32:
+        return APEX_F32
+    raise TypeError("tensors must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("apex calls take device tensors")
+    if not t.is_contiguous():
+        raise ValueError("apex calls take contiguous [B, H, S, d_h] tensors")
+    return t.data_ptr()
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check(fn, status):
+    if status != 0:
+        raise ApexError(fn, status)
+
+
+def apex_rope_qk(q, k, q_out=None, k_out=None, m0=0, base=10000.0, stream=None):
+    """RoPE(q) -> q_out and RoPE(k) -> k_out; an output left None means in place.
+    q [B,H_q,S,d_h] or None, k [B,H_kv,S,d_h] or None."""
+    if q is not None and q_out is None:
+        q_out = q
+    if k is not None and k_out is None:
+        k_out = k
+    t = q if q is not None else k
+    B, _, S, d = t.shape
+    Hq = q.shape[1] if q is not None else 0
+    Hkv = k.shape[1] if k is not None else 0
+    _check("apex_rope_qk", lib().apex_rope_qk(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), B, S,
+                                              Hq, Hkv, d, int(m0), float(base), _dtype_code(t),
+                                              _stream(t, stream)))
+
+
+def apex_attn_prefill(q, k, v, o, k_rope_out=None, causal=1, W=0, m0=0, base=10000.0,
+                      apply_rope=1, stream=None):
+    """o = softmax(RoPE(q) RoPE(k)^T / sqrt(d_h)) v. apply_rope: 1 = rotate q and k
+    (RoPE(k) lands in k_rope_out), 2 = rotate q only (k holds rotated keys), 0 = none."""
+    B, Hq, S, d = q.shape
+    Hkv = k.shape[1]
+    _check("apex_attn_prefill",
+           lib().apex_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(k_rope_out), B, S, Hq,
+                                   Hkv, d, int(causal), int(W), int(m0), float(base),
+                                   int(apply_rope), _dtype_code(q), _stream(q, stream)))
+
+
+def apex_attn_decode_workspace_bytes(B, H_q, H_kv, Sk, d_h):
+    return int(lib().apex_attn_decode_workspace_bytes(B, H_q, H_kv, Sk, d_h))
+
+
+def apex_attn_decode(q, k_cache, v_cache, k_new, v_new, o, m, W=0, base=10000.0, apply_rope=1,
+                     workspace=None, stream=None):
+    """One query per (b, h) at position m against [B,H_kv,Sk,d_h] caches."""
+    B, Hq, _, d = q.shape
+    Hkv, Sk = k_cache.shape[1], k_cache.shape[2]
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("apex_attn_decode",
+           lib().apex_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+                                  _ptr(o), B, Sk, Hq, Hkv, d, int(W), int(m), float(base),
+                                  int(apply_rope), _ptr(workspace), nbytes, _dtype_code(q),
+                                  _stream(q, stream)))

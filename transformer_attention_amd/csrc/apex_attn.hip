@@ -1,0 +1,223 @@
+// apex_attn.hip -- host side of the C ABI declared in include/apex_attn.h:
+// argument checks, launch geometry and kernel launches. All work is enqueued
+// on the caller's stream; nothing here allocates, frees or synchronizes.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "apex_attn.h"
+#include "decode_kernel.hpp"
+#include "prefill_f32_kernel.hpp"
+#include "prefill_kernel.hpp"
+#include "rope_kernel.hpp"
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634074;
+
+bool head_size_ok(int d_h) { return d_h == 64 || d_h == 128; }
+
+int check_dims(int d_h, int dtype) {
+  if (d_h < 2 || (d_h & 1)) return APEX_EINVAL;
+  if (dtype != APEX_F32 && dtype != APEX_BF16) return APEX_EINVAL;
+  if (!head_size_ok(d_h)) return APEX_EUNSUPPORTED;
+  return APEX_OK;
+}
+
+int launch_status() {
+  return hipGetLastError() == hipSuccess ? APEX_OK : APEX_EHIP;
+}
+
+int launch_rope(const void* src, void* dst, long long n_bh, int S, int d_h, int64_t m0,
+                double base, int dtype, hipStream_t st) {
+  apex::RopeParams p{src, dst, n_bh, S, d_h, (long long)m0, base};
+  const long long work = n_bh * ((S + apex::kRopeRows - 1) / apex::kRopeRows) * (d_h / 8);
+  long long blocks = (work + apex::kRopeThreads - 1) / apex::kRopeThreads;
+  if (blocks > 65535LL * 16) blocks = 65535LL * 16;
+  if (blocks < 1) blocks = 1;
+  if (dtype == APEX_BF16)
+    hipLaunchKernelGGL(apex::rope_kernel<uint16_t>, dim3((unsigned)blocks), dim3(apex::kRopeThreads),
+                       0, st, p);
+  else
+    hipLaunchKernelGGL(apex::rope_kernel<float>, dim3((unsigned)blocks), dim3(apex::kRopeThreads), 0,
+                       st, p);
+  return launch_status();
+}
+
+// Largest power of two that divides G, capped at the 8 waves of a workgroup.
+int head_pack(int G) {
+  int gp = 1;
+  while (gp < 8 && G % (gp * 2) == 0) gp *= 2;
+  return gp;
+}
+
+// Split-K geometry of the decode: workgroups per (b, KV head, head block).
+int decode_splits(int B, int Hkv, int n_hb, int Sk) {
+  const long long groups = (long long)B * Hkv * n_hb;
+  long long want = (1024 + groups - 1) / groups;        // about 4 workgroups per CU
+  const long long cap = (Sk + 4095) / 4096;             // >= 1024 keys per wave
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  return (int)want;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* apex_strerror(int status) {
+  switch (status) {
+    case APEX_OK: return "ok";
+    case APEX_EINVAL: return "invalid argument";
+    case APEX_EUNSUPPORTED: return "unsupported head size or dtype";
+    case APEX_EWORKSPACE: return "decode workspace missing or too small";
+    case APEX_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int apex_rope_qk(const void* q, const void* k, void* q_out, void* k_out, int B, int S, int H_q,
+                 int H_kv, int d_h, int64_t m0, double base, int dtype, void* stream) {
+  if ((q == nullptr) != (q_out == nullptr) || (k == nullptr) != (k_out == nullptr) || (!q && !k))
+    return APEX_EINVAL;
+  if (B < 1 || S < 1 || (q && H_q < 1) || (k && H_kv < 1) || m0 < 0 || !(base > 0.0))
+    return APEX_EINVAL;
+  const int dc = check_dims(d_h, dtype);
+  if (dc != APEX_OK) return dc;
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  int rc = APEX_OK;
+  if (q) rc = launch_rope(q, q_out, (long long)B * H_q, S, d_h, m0, base, dtype, st);
+  if (rc == APEX_OK && k) rc = launch_rope(k, k_out, (long long)B * H_kv, S, d_h, m0, base, dtype, st);
+  return rc;
+}
+
+int apex_attn_prefill(const void* q, const void* k, const void* v, void* o, void* k_rope_out,
+                      int B, int S, int H_q, int H_kv, int d_h, int causal, int W, int64_t m0,
+                      double base, int apply_rope, int dtype, void* stream) {
+  if (!q || !k || !v || !o || (apply_rope == 1 && !k_rope_out)) return APEX_EINVAL;
+  if (B < 1 || S < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0) return APEX_EINVAL;
+  if (W < 0 || (W > 0 && !causal) || (causal != 0 && causal != 1)) return APEX_EINVAL;
+  if (m0 < 0 || apply_rope < 0 || apply_rope > 2 || (apply_rope && !(base > 0.0)))
+    return APEX_EINVAL;
+  const int dc = check_dims(d_h, dtype);
+  if (dc != APEX_OK) return dc;
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+
+  const void* kr = k;
+  if (apply_rope == 1) {
+    const int rc = launch_rope(k, k_rope_out, (long long)B * H_kv, S, d_h, m0, base, dtype, st);
+    if (rc != APEX_OK) return rc;
+    kr = k_rope_out;
+  }
+  const int G = H_q / H_kv;
+  if (dtype == APEX_BF16) {
+    apex::PrefillParams p{};
+    p.q = (const uint16_t*)q;
+    p.k = (const uint16_t*)kr;
+    p.v = (const uint16_t*)v;
+    p.o = (uint16_t*)o;
+    p.S = S; p.Hq = H_q; p.Hkv = H_kv; p.G = G;
+    p.causal = causal; p.W = W; p.m0 = m0; p.base = base; p.apply_rope = apply_rope != 0;
+    p.g_pack = head_pack(G);
+    p.bm = apex::kPfRows / p.g_pack;
+    p.n_pos_tiles = (S + p.bm - 1) / p.bm;
+    p.n_head_packs = G / p.g_pack;
+    p.n_groups = B * H_kv * p.n_head_packs;
+    p.sc = (float)(kLog2e / sqrt((double)d_h));
+    const long long blocks = (long long)p.n_pos_tiles * p.n_groups;
+    if (blocks > 0x7fffffffLL) return APEX_EUNSUPPORTED;
+    if (d_h == 128)
+      hipLaunchKernelGGL(apex::prefill_bf16_kernel<128>, dim3((unsigned)blocks),
+                         dim3(apex::kPfThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL(apex::prefill_bf16_kernel<64>, dim3((unsigned)blocks),
+                         dim3(apex::kPfThreads), 0, st, p);
+  } else {
+    apex::PrefillF32Params p{};
+    p.q = (const float*)q;
+    p.k = (const float*)kr;
+    p.v = (const float*)v;
+    p.o = (float*)o;
+    p.S = S; p.Hq = H_q; p.Hkv = H_kv; p.G = G;
+    p.causal = causal; p.W = W; p.m0 = m0; p.base = base; p.apply_rope = apply_rope != 0;
+    p.scale = (float)(1.0 / sqrt((double)d_h));
+    if (B > 65535 || H_q > 65535) return APEX_EUNSUPPORTED;
+    const dim3 grid((S + apex::kF32Rows - 1) / apex::kF32Rows, H_q, B);
+    if (d_h == 128)
+      hipLaunchKernelGGL(apex::prefill_f32_kernel<128>, grid, dim3(apex::kF32Threads), 0, st, p);
+    else
+      hipLaunchKernelGGL(apex::prefill_f32_kernel<64>, grid, dim3(apex::kF32Threads), 0, st, p);
+  }
+  return launch_status();
+}
+
+size_t apex_attn_decode_workspace_bytes(int B, int H_q, int H_kv, int Sk, int d_h) {
+  if (B < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || Sk < 1 || d_h < 2) return 0;
+  const int G = H_q / H_kv;
+  const int n_hb = (G + apex::kDecHeads - 1) / apex::kDecHeads;
+  const int n_parts = decode_splits(B, H_kv, n_hb, Sk) * apex::kDecWaves;
+  return (size_t)B * H_q * n_parts * (size_t)(d_h + 2) * sizeof(float);
+}
+
+int apex_attn_decode(const void* q, void* k_cache, void* v_cache, const void* k_new,
+                     const void* v_new, void* o, int B, int Sk, int H_q, int H_kv, int d_h, int W,
+                     int64_t m, double base, int apply_rope, void* workspace,
+                     size_t workspace_bytes, int dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !o || ((k_new == nullptr) != (v_new == nullptr)))
+    return APEX_EINVAL;
+  if (B < 1 || Sk < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || W < 0) return APEX_EINVAL;
+  if (m < 0 || m >= Sk || (apply_rope != 0 && apply_rope != 1) || (apply_rope && !(base > 0.0)))
+    return APEX_EINVAL;
+  const int dc = check_dims(d_h, dtype);
+  if (dc != APEX_OK) return dc;
+  if (dtype != APEX_BF16) return APEX_EUNSUPPORTED;
+  const size_t need = apex_attn_decode_workspace_bytes(B, H_q, H_kv, Sk, d_h);
+  if (!workspace || workspace_bytes < need) return APEX_EWORKSPACE;
+  if (B > 65535) return APEX_EUNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+
+  const int G = H_q / H_kv;
+  const int n_hb = (G + apex::kDecHeads - 1) / apex::kDecHeads;
+  const int n_split = decode_splits(B, H_kv, n_hb, Sk);
+  const int n_parts = n_split * apex::kDecWaves;
+  const long long key_lo = W > 0 ? (m - W + 1 > 0 ? m - W + 1 : 0) : 0;
+  const long long n_keys = m - key_lo + 1;
+  long long kpp = (n_keys + n_parts - 1) / n_parts;
+  kpp = (kpp + apex::kDecBN - 1) / apex::kDecBN * apex::kDecBN;
+
+  apex::DecodeParams p{};
+  p.q = (const uint16_t*)q;
+  p.kc = (uint16_t*)k_cache;
+  p.vc = (uint16_t*)v_cache;
+  p.kn = (const uint16_t*)k_new;
+  p.vn = (const uint16_t*)v_new;
+  p.ws_o = (float*)workspace;
+  p.ws_ml = p.ws_o + (size_t)B * H_q * n_parts * d_h;
+  p.Sk = Sk; p.Hq = H_q; p.Hkv = H_kv; p.G = G;
+  p.m = m; p.base = base; p.apply_rope = apply_rope;
+  p.n_hb = n_hb; p.n_parts = n_parts;
+  p.key_lo = (int)key_lo;
+  p.keys_per_part = (int)kpp;
+  p.sc = (float)(kLog2e / sqrt((double)d_h));
+  const dim3 grid(n_split, H_kv * n_hb, B);
+  if (d_h == 128)
+    hipLaunchKernelGGL(apex::decode_split_kernel<128>, grid, dim3(apex::kDecThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL(apex::decode_split_kernel<64>, grid, dim3(apex::kDecThreads), 0, st, p);
+  int rc = launch_status();
+  if (rc != APEX_OK) return rc;
+
+  apex::CombineParams c{p.ws_o, p.ws_ml, (uint16_t*)o, B * H_q, n_parts};
+  const dim3 cgrid((B * H_q + 3) / 4);
+  if (d_h == 128)
+    hipLaunchKernelGGL(apex::decode_combine_kernel<128>, cgrid, dim3(256), 0, st, c);
+  else
+    hipLaunchKernelGGL(apex::decode_combine_kernel<64>, cgrid, dim3(256), 0, st, c);
+  return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// device_common.hpp -- gfx950 building blocks shared by the RoPE, prefill and
+// decode kernels: vector types, bf16 packing, MFMA wrappers, the transposing
+// LDS read, and the RoPE angle evaluation.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace apex {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+#define APEX_LDS __attribute__((address_space(3)))
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr double kInvTwoPi = 0.15915494309189533576888376337251436;  // 1 / (2 pi)
+
+// ---- bf16 <-> fp32 -------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// Round two fp32 values to bf16 (nearest even) and pack them, a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  f32x2 f = {a, b};
+  bf16x2 h = __builtin_convertvector(f, bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float a) {
+  return __builtin_bit_cast(uint16_t, (__bf16)a);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// ---- MFMA ------------------------------------------------------------------
+// v_mfma_f32_32x32x16_bf16. Lane l supplies A[l%32][8(l/32)+e] and
+// B[8(l/32)+e][l%32], e = 0..7; D[8(r/4)+4(l/32)+r%4][l%32] lands in reg r.
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+// v_mfma_f32_16x16x32_bf16. Lane l supplies A[l%16][8(l/16)+e] and
+// B[8(l/16)+e][l%16]; D[4(l/16)+r][l%16] lands in reg r.
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane j names an 8-byte
+// chunk (4 bf16); lane i receives element i%4 of the chunks named by lanes
+// i/4, 4+i/4, 8+i/4, 12+i/4. When lane j points at row (r0 + j/4), columns
+// c0 + 4(j%4) .. +3 of a row-major LDS matrix, lane i receives the column
+// c0 + i over the rows r0 .. r0+3: a 4x16 transpose.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((APEX_LDS i16x4*)(APEX_LDS void*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// ---- RoPE angles -------------------------------------------------------------
+// turns_i = theta_i / (2 pi) with theta_i = b^(-2i/d_h) (fp64).
+__device__ __forceinline__ double rope_turns(int i, int d_h, double base) {
+  return pow(base, -2.0 * (double)i / (double)d_h) * kInvTwoPi;
+}
+// The angle pos * theta_i is formed in fp64 as turns and reduced to [-1/2, 1/2]
+// before any fp32 step, so large positions lose no accuracy.
+__device__ __forceinline__ float reduced_turns(int64_t pos, double turns) {
+  double t = (double)pos * turns;
+  return (float)(t - rint(t));
+}
+// Accurate fp32 cos / sin of the reduced angle (used where outputs stay fp32).
+__device__ __forceinline__ void rope_cs_accurate(int64_t pos, double turns, float& c, float& s) {
+  float x = 2.0f * reduced_turns(pos, turns);  // angle / pi in [-1, 1]
+  sincospif(x, &s, &c);
+}
+// Hardware sine / cosine of the reduced angle (v_sin_f32 / v_cos_f32 take
+// turns), used where the rotated value is rounded to bf16 right after.
+__device__ __forceinline__ void rope_cs_fast(int64_t pos, double turns, float& c, float& s) {
+  float x = reduced_turns(pos, turns);
+  s = __builtin_amdgcn_sinf(x);
+  c = __builtin_amdgcn_cosf(x);
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+}  // namespace apex

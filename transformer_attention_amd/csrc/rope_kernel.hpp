@@ -1,0 +1,104 @@
+// rope_kernel.hpp -- standalone rotary position embedding over [B, H, S, d_h]
+// (APEX-1 Mathematical Reference, Part 1, §4.2 "Core Idea", §4.3 "Frequency
+// Formula", §4.4 "Compact Form" with adjacent pairs (2i, 2i+1)).
+//
+// HBM-bound elementwise pass. A thread owns one 8-element chunk (4 pairs) of
+// the head vector for kRopeRows consecutive positions of one (b, h): it forms
+// cos/sin of p*theta_i exactly (fp64 turns, accurate fp32 sincos) for the first
+// position and steps to the next positions by one complex multiplication with
+// (cos theta_i, sin theta_i), so the trigonometry is paid once per chunk of rows.
+// Consecutive threads cover consecutive chunks of a row, so a wave reads and
+// writes whole rows (coalesced 16- or 32-byte accesses).
+#pragma once
+#include "device_common.hpp"
+
+namespace apex {
+
+constexpr int kRopeRows = 16;
+constexpr int kRopeThreads = 256;
+
+struct RopeParams {
+  const void* src;
+  void* dst;           // may equal src
+  long long n_bh;      // B * H
+  int S;
+  int d_h;
+  long long m0;
+  double base;
+};
+
+template <typename T>
+struct RopeIO;
+
+template <>
+struct RopeIO<uint16_t> {  // bf16: 8 elements = 16 bytes
+  static __device__ __forceinline__ void load(const void* p, size_t off, float* x) {
+    u32x4 w = *(const u32x4*)((const uint16_t*)p + off);
+#pragma unroll
+    for (int e = 0; e < 4; e++) { x[2 * e] = bf16_lo(w[e]); x[2 * e + 1] = bf16_hi(w[e]); }
+  }
+  static __device__ __forceinline__ void store(void* p, size_t off, const float* x) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; e++) w[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+    *(u32x4*)((uint16_t*)p + off) = w;
+  }
+};
+
+template <>
+struct RopeIO<float> {  // fp32: 8 elements = 32 bytes
+  static __device__ __forceinline__ void load(const void* p, size_t off, float* x) {
+    const f32x4* s = (const f32x4*)((const float*)p + off);
+    f32x4 a = s[0], b = s[1];
+#pragma unroll
+    for (int e = 0; e < 4; e++) { x[e] = a[e]; x[4 + e] = b[e]; }
+  }
+  static __device__ __forceinline__ void store(void* p, size_t off, const float* x) {
+    f32x4* d = (f32x4*)((float*)p + off);
+    d[0] = f32x4{x[0], x[1], x[2], x[3]};
+    d[1] = f32x4{x[4], x[5], x[6], x[7]};
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeParams p) {
+  __shared__ double turns_lds[128];  // theta_i / (2 pi), i < d_h / 2 <= 128
+  if ((int)threadIdx.x < p.d_h / 2) turns_lds[threadIdx.x] = rope_turns(threadIdx.x, p.d_h, p.base);
+  __syncthreads();
+  const int chunks = p.d_h >> 3;
+  const int row_blocks = (p.S + kRopeRows - 1) / kRopeRows;
+  const long long total = p.n_bh * row_blocks * chunks;
+  for (long long t = blockIdx.x * (long long)kRopeThreads + threadIdx.x; t < total;
+       t += (long long)gridDim.x * kRopeThreads) {
+    const int ch = (int)(t % chunks);
+    const long long rb_all = t / chunks;
+    const int rb = (int)(rb_all % row_blocks);
+    const long long bh = rb_all / row_blocks;
+    const int s0 = rb * kRopeRows;
+    float c[4], s[4], cs[4], ss[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const double turns = turns_lds[ch * 4 + e];
+      rope_cs_accurate(p.m0 + s0, turns, c[e], s[e]);
+      rope_cs_accurate(1, turns, cs[e], ss[e]);  // one-position step
+    }
+    const int rows = min(kRopeRows, p.S - s0);
+    for (int r = 0; r < rows; r++) {
+      const size_t off = ((size_t)bh * p.S + s0 + r) * p.d_h + ch * 8;
+      float x[8];
+      RopeIO<T>::load(p.src, off, x);
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const float a = x[2 * e], b = x[2 * e + 1];
+        x[2 * e] = a * c[e] - b * s[e];
+        x[2 * e + 1] = a * s[e] + b * c[e];
+        const float cn = c[e] * cs[e] - s[e] * ss[e];
+        s[e] = c[e] * ss[e] + s[e] * cs[e];
+        c[e] = cn;
+      }
+      RopeIO<T>::store(p.dst, off, x);
+    }
+  }
+}
+
+}  // namespace apex
