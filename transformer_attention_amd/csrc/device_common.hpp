@@ -60,6 +60,16 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// global_load_lds_dwordx4: each lane copies 16 bytes from its global address
+// straight into LDS at lds_base + 16 * lane (lds_base wave-uniform), without
+// passing through registers. The builtin exists only for the device target, so
+// the host pass of this file (which only emits launch stubs) does not see it.
+__device__ __forceinline__ void global_to_lds16(const void* src, APEX_LDS void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+#endif
+}
+
 // ---- RoPE angles -------------------------------------------------------------
 // turns_i = theta_i / (2 pi) with theta_i = b^(-2i/d_h) (fp64).
 __device__ __forceinline__ double rope_turns(int i, int d_h, double base) {

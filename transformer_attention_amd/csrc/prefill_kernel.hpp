@@ -9,7 +9,7 @@
 //   Each wave owns 32 rows (one head, 32 positions). K/V tiles of 64 keys are
 //   staged once in LDS and reused by all 8 waves, i.e. by all g_pack heads.
 //   Tiles are visited only inside the rows' visible key range; per wave a
-//   tile is skipped, computed without a mask, or masked element by element.
+//   tile is computed without a mask or masked element by element.
 //   Workgroups are numbered longest-first (latest positions first) and the
 //   (batch, KV head) group varies fastest, so one group's workgroups land on
 //   one XCD (workgroup i runs on XCD i mod 8) and share its L2.
@@ -23,9 +23,20 @@
 //   O^T += V^T P^T (keys as the contraction), and V^T comes from LDS through
 //   the transposing ds_read_b64_tr_b16. O^T keeps one query row per lane.
 //
+// Pipeline (one barrier per 64-key tile)
+//   K and V tiles go from HBM/L2 straight into LDS (global_load_lds_dwordx4,
+//   no registers in between). Tile t's iteration issues the loads of V(t+1)
+//   and K(t+2), computes S(t+1) = K(t+1) Q^T on the matrix cores while the
+//   vector ALUs run the softmax of S(t), then accumulates P(t) V(t).
+//   LDS rows are unpadded; 16-byte chunks are XOR-swizzled per row so that
+//   both the K reads (16 rows, same chunk) and the transposed V reads (4 rows
+//   x 4 chunks per half wave) hit distinct banks.
+//
 // Online softmax (fp32): scores are scaled by log2(e)/sqrt(d_h) so exp2 can
-// be used; a running max m and sum l per row; O and l are rescaled by
-// exp2(m_old - m_new) when the max grows.
+// be used. The running max m only moves when a tile's max exceeds it by more
+// than 8 (in log2 units): probabilities stay <= 2^8, and O and the running
+// sum l are rescaled by exp2(m_old - m_new) only then. O / l is exact for any
+// such choice of m.
 #pragma once
 #include "device_common.hpp"
 
@@ -35,8 +46,7 @@ constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * 64;
 constexpr int kPfRows = kPfWaves * 32;  // query rows per workgroup
 constexpr int kPfBN = 64;               // keys per K/V tile
-constexpr int kPfKPad = 8;              // bf16 pad per K row in LDS (16 B)
-constexpr int kPfVPad = 32;             // bf16 pad per V row in LDS (64 B)
+constexpr float kLazyMax = 8.0f;        // log2 headroom before the max moves
 
 struct PrefillParams {
   const uint16_t* q;
@@ -56,32 +66,34 @@ struct PrefillParams {
   float sc;           // log2(e) / sqrt(d_h)
 };
 
-enum TileClass { kSkip = 0, kFull = 1, kPartial = 2 };
+// Physical 16-byte chunk of logical chunk c in LDS row r.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);  // 16 chunks per row
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);           // 8 chunks per row
+}
 
-// Classify keys [j0, j0 + kPfBN) against rows [r0, r0 + 32) (Part 2, §10.2).
-__device__ __forceinline__ int classify_tile(int j0, int r0, int S, int causal, int W) {
+// True when every key of [j0, j0 + kPfBN) is visible to every row of
+// [r0, r0 + 32) (Part 2, §10.2), so the tile needs no mask.
+// Bitwise, not short-circuit, so that it adds no branch to the loop body.
+__device__ __forceinline__ bool tile_is_full(int j0, int r0, int S, int causal, int W) {
   const int j1 = j0 + kPfBN - 1;
-  if (!causal) return j1 < S ? kFull : kPartial;
-  if (j0 > r0 + 31) return kSkip;                  // every key after every row
-  if (W > 0 && j1 <= r0 - W) return kSkip;         // every key outside every window
-  const bool below = j1 <= r0;                     // j <= i for all pairs
-  const bool inside = W == 0 || j0 >= r0 + 32 - W; // i - j < W for all pairs
-  return (below && inside && j1 < S) ? kFull : kPartial;
+  return (j1 < S) & ((causal == 0) | ((j1 <= r0) & ((W == 0) | (j0 >= r0 + 32 - W))));
 }
 
 template <int D>
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_bf16_kernel(PrefillParams p) {
   static_assert(D == 64 || D == 128, "head size");
-  constexpr int KS = D + kPfKPad;   // LDS row strides (elements)
-  constexpr int VS = D + kPfVPad;
-  constexpr int KK = D / 16;        // MFMA steps over the head dimension
-  constexpr int DB = D / 32;        // 32-wide blocks of the head dimension
-  constexpr int CHUNKS = kPfBN * D / 8;            // 16-byte chunks per tile
-  constexpr int REP = CHUNKS / kPfThreads;         // chunks per thread per tile
-  static_assert(REP >= 1 && CHUNKS % kPfThreads == 0, "tile split");
+  constexpr int RB = D * 2;                       // bytes per LDS row
+  constexpr int TILE = kPfBN * RB;                // bytes per K or V tile
+  constexpr int LOADS = TILE / 1024 / kPfWaves;   // 1 KB direct loads per wave per tile
+  constexpr int ROWS_PER_LOAD = 1024 / RB;
+  constexpr int KK = D / 16;                      // MFMA steps over the head dimension
+  constexpr int DB = D / 32;                      // 32-wide blocks of the head dimension
+  static_assert(LOADS >= 1, "tile split");
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kPfBN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kPfBN * VS];
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[2][TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf[2][TILE];
   __shared__ double turns_lds[D / 2];
 
   const int tid = threadIdx.x;
@@ -103,10 +115,43 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_bf16_kernel(PrefillPara
   const int pw = p0 + (wave % pos_blocks) * 32;
   const int row = pw + r32;  // this lane's query row
 
-  if (p.apply_rope) {
-    if (tid < D / 2) turns_lds[tid] = rope_turns(tid, D, p.base);
-    __syncthreads();
+  // ---- key range of the workgroup ----
+  int j_lo = 0, j_hi = p.S - 1;
+  if (p.causal) {
+    j_hi = min(p.S - 1, p0 + p.bm - 1);
+    if (p.W > 0) j_lo = max(0, p0 - p.W + 1);
   }
+  const int t_lo = j_lo / kPfBN, t_hi = j_hi / kPfBN;
+
+  const uint16_t* kg = p.k + ((size_t)b * p.Hkv + kvh) * p.S * D;
+  const uint16_t* vg = p.v + ((size_t)b * p.Hkv + kvh) * p.S * D;
+
+  // ---- direct HBM -> LDS tile loads: lane order = physical LDS order ----
+  int ld_row[LOADS], ld_col[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; i++) {
+    const int blk = wave + i * kPfWaves;                  // 1 KB block of the tile
+    const int r = blk * ROWS_PER_LOAD + lane / (RB / 16);
+    const int pc = lane % (RB / 16);
+    ld_row[i] = r;
+    ld_col[i] = (pc ^ swz<D>(r)) * 8;                     // logical chunk, in elements
+  }
+  auto issue_tile = [&](const uint16_t* src, unsigned char* dst, int t) {
+#pragma unroll
+    for (int i = 0; i < LOADS; i++) {
+      const int j = min(t * kPfBN + ld_row[i], p.S - 1);  // rows past S: any valid row
+      global_to_lds16(src + (size_t)j * D + ld_col[i],
+                      (APEX_LDS void*)(dst + (wave + i * kPfWaves) * 1024));
+    }
+  };
+
+  issue_tile(kg, kbuf[0], t_lo);
+  issue_tile(vg, vbuf[0], t_lo);
+  if (t_lo < t_hi) issue_tile(kg, kbuf[1], t_lo + 1);
+
+  if (p.apply_rope && tid < D / 2) turns_lds[tid] = rope_turns(tid, D, p.base);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's tile loads have landed
+  __syncthreads();                                    // ... and every other wave's
 
   // ---- Q^T operand: lane holds row `row`, dims 16kk + 8g .. +7 ----
   u32x4 qf[KK];
@@ -129,135 +174,138 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_bf16_kernel(PrefillPara
     }
   }
 
-  // ---- key range of the workgroup ----
-  int j_lo = 0, j_hi = p.S - 1;
-  if (p.causal) {
-    j_hi = min(p.S - 1, p0 + p.bm - 1);
-    if (p.W > 0) j_lo = max(0, p0 - p.W + 1);
+  // ---- per-lane LDS offsets (loop invariant) ----
+  // K operand: row kb*32 + r32, logical chunk 2kk + g.
+  int k_off[KK];
+  {
+    const int sw = swz<D>(r32);
+#pragma unroll
+    for (int kk = 0; kk < KK; kk++) k_off[kk] = r32 * RB + (((2 * kk + g) ^ sw) << 4);
   }
-  const int t_lo = j_lo / kPfBN, t_hi = j_hi / kPfBN;
-
-  const uint16_t* kbase = p.k + ((size_t)b * p.Hkv + kvh) * p.S * D;
-  const uint16_t* vbase = p.v + ((size_t)b * p.Hkv + kvh) * p.S * D;
-
-  u32x4 kreg[REP], vreg[REP];
-  auto load_tile = [&](int t) {
+  // V^T operand via ds_read_b64_tr_b16: lane j16 of 16-lane group qg reads 8 bytes
+  // at row key + j16/4, columns 32db + 16(qg&1) + 4(j16&3): logical chunk
+  // 4db + 2(qg&1) + (j16&3)/2, half (j16&1). Rows +8 give the k-indices 4..7.
+  const int j16 = lane & 15;
+  const int vrow = 4 * g + (j16 >> 2);
+  int v_off[2][DB];
 #pragma unroll
-    for (int r = 0; r < REP; r++) {
-      const int ci = tid + r * kPfThreads;
-      const int krow = ci / (D / 8), col = (ci % (D / 8)) * 8;
-      const int j = t * kPfBN + krow;
-      if (j < p.S) {
-        kreg[r] = *(const u32x4*)(kbase + (size_t)j * D + col);
-        vreg[r] = *(const u32x4*)(vbase + (size_t)j * D + col);
-      } else {
-        kreg[r] = u32x4{0, 0, 0, 0};
-        vreg[r] = u32x4{0, 0, 0, 0};
-      }
+  for (int h = 0; h < 2; h++) {
+    const int r = vrow + 8 * h;
+    const int sw = swz<D>(r);
+#pragma unroll
+    for (int db = 0; db < DB; db++) {
+      const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1);
+      v_off[h][db] = r * RB + ((chunk ^ sw) << 4) + ((j16 & 1) << 3);
+    }
+  }
+
+  auto qk = [&](const unsigned char* kb_lds, f32x16 (&s)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KK; kk++)
+        s[kb] = mfma32(*(const u32x4*)(kb_lds + kb * 32 * RB + k_off[kk]), qf[kk], s[kb]);
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < REP; r++) {
-      const int ci = tid + r * kPfThreads;
-      const int krow = ci / (D / 8), col = (ci % (D / 8)) * 8;
-      *(u32x4*)(&ks[buf][krow * KS + col]) = kreg[r];
-      *(u32x4*)(&vs[buf][krow * VS + col]) = vreg[r];
-    }
-  };
+
+  // visible keys of this lane's row: [vis_lo, vis_hi]
+  const int vis_hi = p.causal ? min(row, p.S - 1) : p.S - 1;
+  const int vis_lo = (p.causal && p.W > 0) ? row - p.W + 1 : 0;
+  const unsigned vis_span = (unsigned)(vis_hi - vis_lo);
 
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; db++) oacc[db] = f32x16{};
   float m_run = kNegInf, l_run = 0.0f;
 
-  load_tile(t_lo);
-  store_tile(0);
-  __syncthreads();
+  f32x16 sa[2], sb[2];
+  qk(kbuf[0], sa);
+  bool full_a = tile_is_full(t_lo * kPfBN, pw, p.S, p.causal, p.W), full_b = true;
+  __syncthreads();  // every wave is done with kbuf[0] before K(t_lo + 2) lands there
 
-  for (int t = t_lo; t <= t_hi; t++) {
-    const int buf = (t - t_lo) & 1;
-    const bool more = t < t_hi;
-    if (more) load_tile(t + 1);  // in flight while this tile computes
+  // One 64-key tile: S(t+1) = K(t+1) Q^T is issued to the matrix cores while
+  // the vector ALUs run the softmax of S(t); then O += P(t) V(t).
+  auto step = [&](int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2], bool& full_cur,
+                  bool& full_next) {
+    const int it = t - t_lo;
+    if (t + 1 <= t_hi) issue_tile(vg, vbuf[(it + 1) & 1], t + 1);
+    if (t + 2 <= t_hi) issue_tile(kg, kbuf[it & 1], t + 2);
 
-    const int j0 = t * kPfBN;
-    const int cls = classify_tile(j0, pw, p.S, p.causal, p.W);
-    if (cls != kSkip) {
-      // S^T = K Q^T for keys j0 .. j0+63 (two 32-key blocks)
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; kb++) {
-        sacc[kb] = f32x16{};
-        const uint16_t* krow = &ks[buf][(kb * 32 + r32) * KS + 8 * g];
-#pragma unroll
-        for (int kk = 0; kk < KK; kk++)
-          sacc[kb] = mfma32(*(const u32x4*)(krow + 16 * kk), qf[kk], sacc[kb]);
-      }
-      if (cls == kPartial) {
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) {
-            const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            bool vis = j < p.S;
-            if (p.causal) vis = vis && j <= row && (p.W == 0 || row - j < p.W);
-            if (!vis) sacc[kb][r] = kNegInf;
-          }
-      }
-      // row max over this lane's 32 keys and the partner lane's 32 keys
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) mx = fmaxf(mx, sacc[kb][r]);
-      mx = wave_max_xor(mx, 32);
-      const float m_new = fmaxf(m_run, mx * p.sc);
-      const float m_use = m_new == kNegInf ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float lsum = 0.0f;
+    if (!full_cur) {  // per-element mask of tile t
+      const int base = t * kPfBN + 4 * g - vis_lo;
 #pragma unroll
       for (int kb = 0; kb < 2; kb++)
 #pragma unroll
         for (int r = 0; r < 16; r++) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], p.sc, -m_use));
-          sacc[kb][r] = e;
-          lsum += e;
+          const unsigned off = (unsigned)(base + kb * 32 + 8 * (r >> 2) + (r & 3));
+          s_cur[kb][r] = off <= vis_span ? s_cur[kb][r] : kNegInf;
         }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
+    }
+
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) mx = fmaxf(mx, s_cur[kb][r]);
+    mx = wave_max_xor(mx, 32) * p.sc;
+    // the max moves (for every lane of the wave) only when some lane's tile max
+    // exceeds its running max by more than kLazyMax
+    const bool grow = __builtin_amdgcn_ballot_w64(mx > m_run + kLazyMax) != 0;
+    const float m_new = grow ? fmaxf(m_run, mx) : m_run;
+    const float m_use = m_new == kNegInf ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+
+    // S(t+1): on the last tile this reads a stale buffer and is discarded
+    qk(kbuf[(it + 1) & 1], s_next);
+    full_next = tile_is_full((t + 1) * kPfBN, pw, p.S, p.causal, p.W);
+
+    float lsum = 0.0f;
+    u32x4 pk[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int c = 0; c < 2; c++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const float e0 =
+              __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][8 * c + 2 * e], p.sc, -m_use));
+          const float e1 =
+              __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][8 * c + 2 * e + 1], p.sc, -m_use));
+          lsum += e0 + e1;
+          pk[kb][c][e] = pack_bf16x2(e0, e1);
+        }
+    // keep the exponentials next to the S(t+1) MFMAs (not sunk past the branch)
+    asm volatile("" ::"v"(pk[0][0]), "v"(pk[0][1]), "v"(pk[1][0]), "v"(pk[1][1]));
+    l_run = l_run * alpha + lsum;
+    if (grow) {  // wave-uniform, rare after the first tiles
 #pragma unroll
       for (int db = 0; db < DB; db++) oacc[db] *= alpha;
+    }
 
-      // P^T as bf16 B operands: block kb, half c covers keys kb*32 + 16c + (0..15)
-      u32x4 pk[2][2];
+    // O^T += V^T P^T. Operand k-index 8g+e <-> key kb*32 + 16c + 4g + e (e < 4)
+    // and kb*32 + 16c + 8 + 4g + (e - 4) (e >= 4), matching the S^T layout.
+    const unsigned char* vb = vbuf[it & 1];
+#pragma unroll
+    for (int db = 0; db < DB; db++)
 #pragma unroll
       for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-        for (int c = 0; c < 2; c++)
-#pragma unroll
-          for (int e = 0; e < 4; e++)
-            pk[kb][c][e] = pack_bf16x2(sacc[kb][8 * c + 2 * e], sacc[kb][8 * c + 2 * e + 1]);
-
-      // O^T += V^T P^T. Operand k-index 8g+e <-> key kb*32 + 16c + 4g + e (e < 4)
-      // and kb*32 + 16c + 8 + 4g + (e - 4) (e >= 4), matching the S^T layout.
-      const int j16 = lane & 15;
-      const int dsub = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
-#pragma unroll
-      for (int db = 0; db < DB; db++) {
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-          for (int c = 0; c < 2; c++) {
-            const int key = kb * 32 + 16 * c + 4 * g + (j16 >> 2);
-            const uint16_t* vp = &vs[buf][key * VS + db * 32 + dsub];
-            const u32x2 lo = lds_read_tr16(vp);
-            const u32x2 hi = lds_read_tr16(vp + 8 * VS);
-            oacc[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pk[kb][c], oacc[db]);
-          }
-      }
-    }
-    if (more) store_tile(buf ^ 1);
+        for (int c = 0; c < 2; c++) {
+          const int koff = (kb * 32 + 16 * c) * RB;
+          const u32x2 lo = lds_read_tr16((const uint16_t*)(vb + koff + v_off[0][db]));
+          const u32x2 hi = lds_read_tr16((const uint16_t*)(vb + koff + v_off[1][db]));
+          oacc[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pk[kb][c], oacc[db]);
+        }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // V(t+1), K(t+2) have landed
     __syncthreads();
+  };
+
+  for (int t = t_lo; t <= t_hi; t += 2) {
+    step(t, sa, sb, full_a, full_b);
+    if (t + 1 > t_hi) break;
+    step(t + 1, sb, sa, full_b, full_a);
   }
 
   // ---- epilogue: O = O^T / l, rounded to bf16 ----
