@@ -153,32 +153,28 @@ def time_decode(taa, torch, steps, warmup):
 
 
 def cpu_baseline(w, budget_s):
-    """Time the fp64 oracle on whole query heads of the workload (all rows of
-    each), as many as fit in about budget_s seconds."""
+    """Time the fp64 oracle over the whole workload (every batch element, head
+    and row, drawn on the host from the same seeds), repeating whole passes
+    until about budget_s seconds have been spent."""
     import apex_inputs
     import oracle
     threads = oracle.default_threads()
     B, S, Hq, Hkv, d = w["B"], w["S"], w["Hq"], w["Hkv"], w["d"]
-    # batch element 0 of the workload's shape, drawn on the host
-    q, k, v = apex_inputs.prefill_inputs(1, S, Hq, Hkv, d, w["dtype"], seed=w["seed"],
+    q, k, v = apex_inputs.prefill_inputs(B, S, Hq, Hkv, d, w["dtype"], seed=w["seed"],
                                          device="cpu")
-    per_head = 4 * d * n_visible(S, w["causal"], w["W"])
+    flops = 4 * d * B * Hq * n_visible(S, w["causal"], w["W"])
     kw = dict(causal=w["causal"], W=w["W"], m0=w["m0"], base=w["base"], nthreads=threads)
-
-    def run(n_heads):
-        rows = [h * S + i for h in range(n_heads) for i in range(S)]
+    passes, t = 0, 0.0
+    while passes == 0 or t < budget_s:
         t0 = time.perf_counter()
-        oracle.prefill(q, k, v, rows=rows, **kw)
-        return time.perf_counter() - t0
-
-    t1 = run(1)
-    n = max(1, min(Hq, int(budget_s / max(t1, 1e-6))))
-    t = run(n) if n > 1 else t1
-    return {"value": round(n * per_head / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+        oracle.prefill(q, k, v, **kw)
+        t += time.perf_counter() - t0
+        passes += 1
+    return {"value": round(passes * flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": "%d query head(s) x all %d rows of %s (one batch element drawn on "
-                      "the host), %.1f s, "
-                      "%.3g GFLOP mask-adjusted" % (n, S, HEADLINE, t, n * per_head / 1e9)}
+            "sample": "%d whole pass(es) over %s (B=%d x %d heads x %d rows, drawn on the "
+                      "host), %.1f s, %.4g GFLOP mask-adjusted per pass"
+                      % (passes, HEADLINE, B, Hq, S, t, flops / 1e9)}
 
 
 def copy_calibration(torch):
@@ -194,6 +190,48 @@ def copy_calibration(torch):
                       "launches": 5}))
 
 
+def _pmc_per_dispatch(csv_path, kernel_substr):
+    """Mean counter value (KiB) per dispatch of the kernels whose name contains
+    kernel_substr, from a rocprofv3 --pmc ... --output-format csv file."""
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if kernel_substr in r["Kernel_Name"]]
+    if not vals:
+        raise ValueError("no %s dispatches in %s" % (kernel_substr, csv_path))
+    return sum(vals) / len(vals), len(vals)
+
+
+def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """Write the prefill kernel's HBM traffic per launch, from FETCH_SIZE and
+    WRITE_SIZE runs scaled by what the same counters read for the calibration
+    copy (read 1 GiB, write 1 GiB), into profiles/ next to the source hash."""
+    f = lambda d: os.path.join(d, "p_counter_collection.csv")
+    kname = "prefill_bf16_kernel<128>"
+    fetch, nf = _pmc_per_dispatch(f(fetch_dir), kname)
+    write, nw = _pmc_per_dispatch(f(write_dir), kname)
+    cf, _ = _pmc_per_dispatch(f(copy_fetch_dir), "neg_kernel")
+    cw, _ = _pmc_per_dispatch(f(copy_write_dir), "neg_kernel")
+    known_kib = (1 << 30) / 1024.0
+    fetch_scale, write_scale = known_kib / cf, known_kib / cw
+    out = {
+        "kernel": kname, "workload": HEADLINE,
+        "fetch_kib_per_dispatch_raw": round(fetch, 1), "write_kib_per_dispatch_raw": round(write, 1),
+        "dispatches": [nf, nw],
+        "copy_calibration": {"known_kib_read": known_kib, "fetch_kib": round(cf, 1),
+                             "known_kib_written": known_kib, "write_kib": round(cw, 1),
+                             "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4)},
+        "hbm_read_bytes_per_launch": int(fetch * fetch_scale * 1024),
+        "hbm_write_bytes_per_launch": int(write * write_scale * 1024),
+        "hbm_bytes_per_launch": int((fetch * fetch_scale + write * write_scale) * 1024),
+        "algorithmic_bytes_per_launch": prefill_bytes(__import__("apex_inputs").WORKLOADS[HEADLINE]),
+        "source_sha": sources_sha(PREFILL_SOURCES),
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,7 +243,12 @@ def main():
                     help="time only the headline prefill (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run the counter-calibration copy kernel and exit")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="rocprofv3 --pmc output dirs -> the prefill traffic summary in profiles/")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
 
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "

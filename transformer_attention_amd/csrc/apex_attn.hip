@@ -45,10 +45,10 @@ int launch_rope(const void* src, void* dst, long long n_bh, int S, int d_h, int6
   return launch_status();
 }
 
-// Largest power of two that divides G, capped at the 8 waves of a workgroup.
+// Largest power of two that divides G, capped at the waves of a workgroup.
 int head_pack(int G) {
   int gp = 1;
-  while (gp < 8 && G % (gp * 2) == 0) gp *= 2;
+  while (gp < apex::kPfWaves && G % (gp * 2) == 0) gp *= 2;
   return gp;
 }
 

@@ -98,4 +98,44 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }
 
+// The value held by lane l ^ 32, through v_permlane32_swap (no LDS round
+// trip): swapping the upper half of one copy with the lower half of another
+// leaves lane l's partner in the first copy for l >= 32, the second for l < 32.
+__device__ __forceinline__ float lane_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// acc + the two bf16 halves of w (v_dot2_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
+// LDS byte address of a __shared__ object, and reads at an LDS byte address.
+// Keeping per-lane base addresses in registers the compiler cannot see through
+// (opaque) lets every buffer/row offset ride in the 16-bit immediate field of
+// the ds_read instructions instead of costing one base register each.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(APEX_LDS const void*)p;
+}
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ u32x4 lds_read16_at(uint32_t addr) {
+  return *(APEX_LDS const u32x4*)(uintptr_t)addr;
+}
+__device__ __forceinline__ u32x2 lds_read_tr16_at(uint32_t addr) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((APEX_LDS i16x4*)(uintptr_t)addr);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+template <int N>
+struct Int {
+  static constexpr int value = N;
+};
+
 }  // namespace apex

@@ -4,10 +4,10 @@
 // §10.2 window mask), Q rotated by RoPE (Part 1, §4.2) as its tile loads.
 //
 // Work decomposition
-//   One workgroup = 8 waves = 256 query rows that all read the same KV head:
-//   g_pack query heads of one GQA group x (256 / g_pack) consecutive positions.
+//   One workgroup = 4 waves = 128 query rows that all read the same KV head:
+//   g_pack query heads of one GQA group x (128 / g_pack) consecutive positions.
 //   Each wave owns 32 rows (one head, 32 positions). K/V tiles of 64 keys are
-//   staged once in LDS and reused by all 8 waves, i.e. by all g_pack heads.
+//   staged once in LDS and reused by all 4 waves, i.e. by all g_pack heads.
 //   Tiles are visited only inside the rows' visible key range; per wave a
 //   tile is computed without a mask or masked element by element.
 //   Workgroups are numbered longest-first (latest positions first) and the
@@ -42,7 +42,10 @@
 
 namespace apex {
 
-constexpr int kPfWaves = 8;
+// Four waves (128 query rows) per workgroup and two workgroups per CU: while
+// one workgroup waits in its prologue (Q and first tiles in flight) or at a
+// barrier, the other one's waves keep the SIMDs busy.
+constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * 64;
 constexpr int kPfRows = kPfWaves * 32;  // query rows per workgroup
 constexpr int kPfBN = 64;               // keys per K/V tile
@@ -58,7 +61,7 @@ struct PrefillParams {
   long long m0;
   double base;
   int apply_rope;     // rotate q while it loads
-  int g_pack;         // query heads per workgroup (divides G, <= 8)
+  int g_pack;         // query heads per workgroup (divides G, <= kPfWaves)
   int bm;             // positions per workgroup = kPfRows / g_pack
   int n_pos_tiles;    // ceil(S / bm)
   int n_head_packs;   // G / g_pack
@@ -82,7 +85,7 @@ __device__ __forceinline__ bool tile_is_full(int j0, int r0, int S, int causal, 
 }
 
 template <int D>
-__global__ __launch_bounds__(kPfThreads, 1) void prefill_bf16_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillParams p) {
   static_assert(D == 64 || D == 128, "head size");
   constexpr int RB = D * 2;                       // bytes per LDS row
   constexpr int TILE = kPfBN * RB;                // bytes per K or V tile
