@@ -276,8 +276,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
               __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][8 * c + 2 * e], p.sc, -m_use));
           const float e1 =
               __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][8 * c + 2 * e + 1], p.sc, -m_use));
-          lsum += e0 + e1;
           pk[kb][c][e] = pack_bf16x2(e0, e1);
+          lsum = add_bf16x2(pk[kb][c][e], lsum);  // the row sum of the rounded P that P V uses
         }
     // keep the exponentials next to the S(t+1) MFMAs (not sunk past the branch)
     asm volatile("" ::"v"(pk[0][0]), "v"(pk[0][1]), "v"(pk[1][0]), "v"(pk[1][1]));
