@@ -70,6 +70,25 @@ __device__ __forceinline__ void global_to_lds16(const void* src, APEX_LDS void* 
 #endif
 }
 
+// buffer_load_dwordx4 ... lds: the same copy as global_to_lds16, addressed
+// through a buffer resource (wave-uniform base and byte size, built on the
+// scalar unit) plus a per-lane byte offset. Lanes whose offset lies at or
+// past the resource's size read zeros instead of memory.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t buffer_rsrc;
+__device__ __forceinline__ buffer_rsrc make_buffer_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer: stride 0, range-checked against `bytes`, 32-bit data format
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void buffer_to_lds16(buffer_rsrc r, uint32_t voffset, APEX_LDS void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, voffset, 0, 0, 0);
+}
+#else
+struct buffer_rsrc {};
+__device__ __forceinline__ buffer_rsrc make_buffer_rsrc(const void*, uint32_t) { return {}; }
+__device__ __forceinline__ void buffer_to_lds16(buffer_rsrc, uint32_t, APEX_LDS void*) {}
+#endif
+
 // ---- RoPE angles -------------------------------------------------------------
 // turns_i = theta_i / (2 pi) with theta_i = b^(-2i/d_h) (fp64).
 __device__ __forceinline__ double rope_turns(int i, int d_h, double base) {

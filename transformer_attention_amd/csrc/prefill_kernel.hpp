@@ -130,22 +130,23 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
   const uint16_t* vg = p.v + ((size_t)b * p.Hkv + kvh) * p.S * D;
 
   // ---- direct HBM -> LDS tile loads: lane order = physical LDS order ----
-  int ld_row[LOADS], ld_col[LOADS];
+  // Byte offset inside a tile of the 16 bytes each lane copies per load.
+  uint32_t ld_off[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; i++) {
     const int blk = wave + i * kPfWaves;                  // 1 KB block of the tile
     const int r = blk * ROWS_PER_LOAD + lane / (RB / 16);
     const int pc = lane % (RB / 16);
-    ld_row[i] = r;
-    ld_col[i] = (pc ^ swz<D>(r)) * 8;                     // logical chunk, in elements
+    ld_off[i] = (uint32_t)(r * RB + ((pc ^ swz<D>(r)) << 4));  // logical chunk of the row
   }
+  // The buffer resource of tile t covers the rows t*kPfBN .. S-1, so rows
+  // past the sequence end arrive as zeros (and are masked anyway).
   auto issue_tile = [&](const uint16_t* src, unsigned char* dst, int t) {
+    const buffer_rsrc r =
+        make_buffer_rsrc(src + (size_t)t * kPfBN * D, (uint32_t)(p.S - t * kPfBN) * RB);
 #pragma unroll
-    for (int i = 0; i < LOADS; i++) {
-      const int j = min(t * kPfBN + ld_row[i], p.S - 1);  // rows past S: any valid row
-      global_to_lds16(src + (size_t)j * D + ld_col[i],
-                      (APEX_LDS void*)(dst + (wave + i * kPfWaves) * 1024));
-    }
+    for (int i = 0; i < LOADS; i++)
+      buffer_to_lds16(r, ld_off[i], (APEX_LDS void*)(dst + (wave + i * kPfWaves) * 1024));
   };
 
   issue_tile(kg, kbuf[0], t_lo);
