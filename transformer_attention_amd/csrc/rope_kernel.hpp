@@ -3,18 +3,19 @@
 // Formula", §4.4 "Compact Form" with adjacent pairs (2i, 2i+1)).
 //
 // HBM-bound elementwise pass. A thread owns one 8-element chunk (4 pairs) of
-// the head vector for kRopeRows consecutive positions of one (b, h): it forms
-// cos/sin of p*theta_i exactly (fp64 turns, accurate fp32 sincos) for the first
-// position and steps to the next positions by one complex multiplication with
-// (cos theta_i, sin theta_i), so the trigonometry is paid once per chunk of rows.
-// Consecutive threads cover consecutive chunks of a row, so a wave reads and
-// writes whole rows (coalesced 16- or 32-byte accesses).
+// the head vector for kRopeRows consecutive positions of one (b, h): it issues
+// all of their loads first, forms cos/sin of p*theta_i exactly (fp64 turns,
+// accurate fp32 sincos) for the first position and steps to the next
+// positions by one complex multiplication with (cos theta_i, sin theta_i),
+// taken from a per-block table, then stores the rows. Consecutive threads
+// cover consecutive chunks of a row, so a wave reads and writes whole rows
+// (coalesced 16- or 32-byte accesses).
 #pragma once
 #include "device_common.hpp"
 
 namespace apex {
 
-constexpr int kRopeRows = 16;
+constexpr int kRopeRows = 4;
 constexpr int kRopeThreads = 256;
 
 struct RopeParams {
@@ -63,7 +64,12 @@ struct RopeIO<float> {  // fp32: 8 elements = 32 bytes
 template <typename T>
 __global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeParams p) {
   __shared__ double turns_lds[128];  // theta_i / (2 pi), i < d_h / 2 <= 128
-  if ((int)threadIdx.x < p.d_h / 2) turns_lds[threadIdx.x] = rope_turns(threadIdx.x, p.d_h, p.base);
+  __shared__ float step_c[128], step_s[128];  // cos, sin of theta_i (one position)
+  if ((int)threadIdx.x < p.d_h / 2) {
+    const double turns = rope_turns(threadIdx.x, p.d_h, p.base);
+    turns_lds[threadIdx.x] = turns;
+    rope_cs_accurate(1, turns, step_c[threadIdx.x], step_s[threadIdx.x]);
+  }
   __syncthreads();
   const int chunks = p.d_h >> 3;
   const int row_blocks = (p.S + kRopeRows - 1) / kRopeRows;
@@ -75,29 +81,31 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeParams p) {
     const int rb = (int)(rb_all % row_blocks);
     const long long bh = rb_all / row_blocks;
     const int s0 = rb * kRopeRows;
-    float c[4], s[4], cs[4], ss[4];
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-      const double turns = turns_lds[ch * 4 + e];
-      rope_cs_accurate(p.m0 + s0, turns, c[e], s[e]);
-      rope_cs_accurate(1, turns, cs[e], ss[e]);  // one-position step
-    }
     const int rows = min(kRopeRows, p.S - s0);
-    for (int r = 0; r < rows; r++) {
-      const size_t off = ((size_t)bh * p.S + s0 + r) * p.d_h + ch * 8;
-      float x[8];
-      RopeIO<T>::load(p.src, off, x);
+    const size_t off0 = ((size_t)bh * p.S + s0) * p.d_h + ch * 8;
+    float x[kRopeRows][8];
+#pragma unroll
+    for (int r = 0; r < kRopeRows; r++)
+      if (r < rows) RopeIO<T>::load(p.src, off0 + (size_t)r * p.d_h, x[r]);
+    float c[4], s[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) rope_cs_accurate(p.m0 + s0, turns_lds[ch * 4 + e], c[e], s[e]);
+#pragma unroll
+    for (int r = 0; r < kRopeRows; r++) {
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        const float a = x[2 * e], b = x[2 * e + 1];
-        x[2 * e] = a * c[e] - b * s[e];
-        x[2 * e + 1] = a * s[e] + b * c[e];
-        const float cn = c[e] * cs[e] - s[e] * ss[e];
-        s[e] = c[e] * ss[e] + s[e] * cs[e];
+        const float a = x[r][2 * e], b = x[r][2 * e + 1];
+        x[r][2 * e] = a * c[e] - b * s[e];
+        x[r][2 * e + 1] = a * s[e] + b * c[e];
+        const float cs = step_c[ch * 4 + e], ss = step_s[ch * 4 + e];
+        const float cn = c[e] * cs - s[e] * ss;
+        s[e] = c[e] * ss + s[e] * cs;
         c[e] = cn;
       }
-      RopeIO<T>::store(p.dst, off, x);
     }
+#pragma unroll
+    for (int r = 0; r < kRopeRows; r++)
+      if (r < rows) RopeIO<T>::store(p.dst, off0 + (size_t)r * p.d_h, x[r]);
   }
 }
 
