@@ -43,9 +43,9 @@ def lib():
         L.apex_oracle_theta.argtypes = [i32, dbl, vp]
         L.apex_oracle_rope_row.argtypes = [vp, vp, i32, i64, dbl]
         L.apex_oracle_rope_row.restype = None
-        L.apex_oracle_visible.argtypes = [i64, i64, i32, i64]
+        L.apex_oracle_visible.argtypes = [i64, i64, i32, i64, i64]
         L.apex_oracle_prefill.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
-                                          i64, dbl, i32, i64, vp, vp, vp, i32]
+                                          i64, i64, dbl, i32, i64, vp, vp, vp, i32]
         L.apex_oracle_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                          i64, dbl, i32, i64, vp, vp, i32]
         _lib = L
@@ -101,14 +101,15 @@ def rope_row(x, pos, base=10000.0):
     return y
 
 
-def visible(i, j, causal, W):
-    return bool(lib().apex_oracle_visible(i, j, int(causal), int(W)))
+def visible(i, j, causal, W, prefix=0):
+    return bool(lib().apex_oracle_visible(i, j, int(causal), int(W), int(prefix)))
 
 
 def prefill(q, k, v, causal=True, W=0, m0=0, base=10000.0, apply_rope=True,
-            rows=None, probs=False, nthreads=None):
+            rows=None, probs=False, nthreads=None, prefix=0):
     """q [B,Hq,S,d]; k, v [B,Hkv,S,d] (float32, or bf16 bits as uint16 / torch bf16).
 
+    prefix: P of the prefix-bidirectional regime (rows i < P see keys j < P).
     rows: optional flat row indices (b*Hq+h)*S+i. Returns fp64 [len(rows), d]
     (or [B,Hq,S,d] when rows is None), and the [.., S] softmax weights if probs."""
     qa, dt = _as_input(q)
@@ -128,7 +129,8 @@ def prefill(q, k, v, causal=True, W=0, m0=0, base=10000.0, apply_rope=True,
     out = np.empty((nrows, d), np.float64)
     pr = np.empty((nrows, S), np.float64) if probs else None
     rc = lib().apex_oracle_prefill(_ptr(qa), _ptr(ka), _ptr(va), dt, B, S, Hq, Hkv, d,
-                                   int(causal), int(W), int(m0), float(base), int(apply_rope),
+                                   int(causal), int(W), int(prefix), int(m0), float(base),
+                                   int(apply_rope),
                                    nrows, _ptr(rarr), _ptr(out), _ptr(pr),
                                    nthreads or default_threads())
     if rc != 0:

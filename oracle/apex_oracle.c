@@ -18,6 +18,9 @@
  *   - GQA: G = H_q/H_kv, query head h reads KV head floor(h/G)  (Part 2, §8.2).
  *   - Window mask: key j is visible to query i iff 0 <= i-j < W and j <= i
  *     (Part 2, §10.2). W = 0 means no window. Non-causal: every key visible.
+ *   - Prefix-bidirectional regime (Part 2, §11.1, picture in §11.3): with a
+ *     prefix of P positions, a query i < P sees exactly the keys j < P; the
+ *     other queries keep the causal (and window) mask. P = 0: no prefix.
  *
  * Readings taken where the pages leave a step open:
  *   - Prefill row s of Q and K sits at position m0 + s; the mask uses i - j only.
@@ -68,8 +71,9 @@ void apex_oracle_rope_row(const double* x, double* y, int d_h, int64_t pos, doub
 }
 
 /* Visibility of key j to query i  (Part 2, §10.2; causal = j <= i). */
-int apex_oracle_visible(int64_t i, int64_t j, int causal, int64_t W) {
+int apex_oracle_visible(int64_t i, int64_t j, int causal, int64_t W, int64_t P) {
   if (!causal) return 1;
+  if (i < P) return j < P;
   if (j > i) return 0;
   if (W > 0 && !(i - j < W)) return 0;
   return 1;
@@ -127,7 +131,7 @@ static void parallel_for(int64_t n, int nthreads, range_fn fn, void* ctx) {
 typedef struct {
   const void *q, *k, *v;
   int dtype, S, Hq, Hkv, d, causal, W, apply_rope;
-  int64_t m0;
+  int64_t P, m0;
   double base;
   int b, kvh;
   double *krot, *vd;          /* [S, d] rotated keys and widened values of the group */
@@ -167,7 +171,7 @@ static void prefill_rows(void* p, int64_t lo, int64_t hi) {
     if (c->apply_rope) apex_oracle_rope_row(q, q, c->d, c->m0 + i, c->base);
     int64_t n = 0;
     for (int64_t j = 0; j < c->S; j++) {
-      if (!apex_oracle_visible(i, j, c->causal, c->W)) continue;
+      if (!apex_oracle_visible(i, j, c->causal, c->W, c->P)) continue;
       keys[n] = c->krot + j * c->d;
       vals[n] = c->vd + j * c->d;
       idx[n] = j;
@@ -187,16 +191,17 @@ static void prefill_rows(void* p, int64_t lo, int64_t hi) {
 /* Attention output rows of a prefill. q [B,Hq,S,d], k and v [B,Hkv,S,d]
  * (row-major, fp32 or bf16 bits). rows: flat indices (b*Hq+h)*S+i of the rows
  * to compute, or NULL for all rows in order. out: [nrows, d] doubles.
- * probs: optional [nrows, S] softmax weights (0 for masked keys).
+ * P: prefix length (0: none; needs causal). probs: optional [nrows, S]
+ * softmax weights (0 for masked keys).
  * Returns 0, or -1 on invalid arguments. */
 int apex_oracle_prefill(const void* q, const void* k, const void* v, int dtype,
                         int B, int S, int Hq, int Hkv, int d, int causal, int W,
-                        int64_t m0, double base, int apply_rope,
+                        int64_t P, int64_t m0, double base, int apply_rope,
                         int64_t nrows, const int64_t* rows, double* out, double* probs,
                         int nthreads) {
   if (!q || !k || !v || !out || B < 1 || S < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv ||
-      d < 2 || (d & 1) || W < 0 || (W > 0 && !causal) || (dtype != 0 && dtype != 1) ||
-      (apply_rope && !(base > 0.0)))
+      d < 2 || (d & 1) || W < 0 || (W > 0 && !causal) || P < 0 || (P > 0 && !causal) ||
+      (dtype != 0 && dtype != 1) || (apply_rope && !(base > 0.0)))
     return -1;
   int64_t total = (int64_t)B * Hq * S;
   if (!rows) nrows = total;
@@ -218,7 +223,7 @@ int apex_oracle_prefill(const void* q, const void* k, const void* v, int dtype,
         if (bh / Hq == b && (bh % Hq) / G == kvh) { all[n] = f; slot[n] = r; n++; }
       }
       if (n == 0) continue;
-      prefill_ctx c = {q, k, v, dtype, S, Hq, Hkv, d, causal, W, apply_rope, m0, base,
+      prefill_ctx c = {q, k, v, dtype, S, Hq, Hkv, d, causal, W, apply_rope, P, m0, base,
                        b, kvh, krot, vd, all, slot, out, probs};
       parallel_for(S, nthreads, prefill_prepare_keys, &c);
       parallel_for(n, nthreads, prefill_rows, &c);
@@ -257,7 +262,7 @@ static void decode_rows(void* p, int64_t lo, int64_t hi) {
     int64_t kv_row0 = (b * c->Hkv + kvh) * (int64_t)c->Sk;
     int64_t n = 0;
     for (int64_t j = 0; j <= c->m; j++) {
-      if (!apex_oracle_visible(c->m, j, 1, c->W)) continue;
+      if (!apex_oracle_visible(c->m, j, 1, c->W, 0)) continue;
       double* kr = kd + n * d;
       double* vr = vd + n * d;
       if (j == c->m && c->kn) {

@@ -28,9 +28,11 @@ def rope(x, pos, base=10000.0):
     return y
 
 
-def visible(i, j, causal, W):
+def visible(i, j, causal, W, P=0):
     if not causal:
         return True
+    if i < P:  # prefix-bidirectional regime
+        return j < P
     return j <= i and (W == 0 or i - j < W)
 
 
@@ -51,7 +53,7 @@ def sdpa(Q, K, V):
     return [sdpa_row(q, K, V)[0] for q in Q]
 
 
-def prefill(q, k, v, causal=True, W=0, m0=0, base=10000.0, apply_rope=True):
+def prefill(q, k, v, causal=True, W=0, m0=0, base=10000.0, apply_rope=True, P=0):
     """q[B][Hq][S][d], k and v [B][Hkv][S][d] -> o[B][Hq][S][d]."""
     B, Hq, S = len(q), len(q[0]), len(q[0][0])
     Hkv = len(k[0])
@@ -66,7 +68,7 @@ def prefill(q, k, v, causal=True, W=0, m0=0, base=10000.0, apply_rope=True):
             rows = []
             for i in range(S):
                 qi = rope(q[b][h][i], m0 + i, base) if apply_rope else q[b][h][i]
-                js = [j for j in range(S) if visible(i, j, causal, W)]
+                js = [j for j in range(S) if visible(i, j, causal, W, P)]
                 o, _ = sdpa_row(qi, [keys[j] for j in js], [v[b][kvh][j] for j in js])
                 rows.append(o)
             heads.append(rows)

@@ -413,3 +413,91 @@ def test_rows_subset_matches_full():
     assert np.array_equal(sub, full.reshape(-1, 16)[rows])
     full_d = oracle.decode(_rand((2, 4, 1, 16)), k, v, None, None, m=30, W=0)
     assert full_d.shape == (2, 4, 1, 16)
+
+
+# --------------------------------------------------------------------------
+# Prefix-bidirectional regime (Part 2, §11.1; picture in §11.3)
+# --------------------------------------------------------------------------
+def test_prefix_mask_matches_page_visual(golden_dir):
+    # Both grids of the picture: prefix P = 4 with full causal rows after it
+    # (global layer), and with a window of 4 after it (local layer).
+    g = _golden(golden_dir, "mask_visual.json")
+    S, P = g["S"], g["prefix"]
+    q, k, v = _rand((1, 1, S, 8)), _rand((1, 1, S, 8)), _rand((1, 1, S, 8))
+    _, pg = oracle.prefill(q, k, v, causal=1, W=0, prefix=P, probs=True)
+    _, pl = oracle.prefill(q, k, v, causal=1, W=g["local_window"], prefix=P, probs=True)
+    for probs in (pg, pl):
+        for row, want in g["prefix_rows"].items():
+            assert list((probs[0, 0, int(row)] > 0).astype(int)) == want
+    for row, want in g["global_causal_rows"].items():
+        assert list((pg[0, 0, int(row)] > 0).astype(int)) == want
+    for row, want in g["local_window_rows"].items():
+        assert list((pl[0, 0, int(row)] > 0).astype(int)) == want
+    # rows 1 and 2 of the prefix, which the picture elides, follow rows 0 and 3
+    for row in (1, 2):
+        assert list((pg[0, 0, row] > 0).astype(int)) == g["prefix_rows"]["0"]
+
+
+@pytest.mark.parametrize("S", [1, 5, 17, 40])
+@pytest.mark.parametrize("P", [0, 1, 3, 16, 39, 40, 55])
+@pytest.mark.parametrize("W", [0, 1, 4])
+def test_prefix_mask_matches_dense_regimes(S, P, W):
+    # A dense S x S mask assembled block by block from the three regimes of
+    # the table: prefix rows see the whole prefix block, the other rows see the
+    # causal lower triangle, cut to a band of width W on local layers.
+    dense = np.zeros((S, S), dtype=bool)
+    Pc = min(P, S)
+    dense[:Pc, :Pc] = True
+    tri = np.tril(np.ones((S, S), dtype=bool))
+    band = tri & ~np.tril(np.ones((S, S), dtype=bool), -W) if W else tri
+    dense[Pc:, :] = band[Pc:, :]
+    for i in range(S):
+        for j in range(S):
+            assert oracle.visible(i, j, 1, W, P) == dense[i, j], (i, j)
+    q, k, v = _rand((1, 1, S, 4)), _rand((1, 1, S, 4)), _rand((1, 1, S, 4))
+    _, pr = oracle.prefill(q, k, v, causal=1, W=W, prefix=P, probs=True)
+    assert np.array_equal(pr[0, 0] > 0, dense)
+
+
+def test_prefix_zero_is_causal_and_prefix_past_end_is_bidirectional():
+    S, d = 23, 8
+    q, k, v = _rand((2, 4, S, d)), _rand((2, 2, S, d)), _rand((2, 2, S, d))
+    for W in (0, 5):
+        assert np.array_equal(oracle.prefill(q, k, v, causal=1, W=W, prefix=0),
+                              oracle.prefill(q, k, v, causal=1, W=W))
+    full = oracle.prefill(q, k, v, causal=0)
+    for P in (S, S + 7):
+        assert np.max(np.abs(oracle.prefill(q, k, v, causal=1, prefix=P) - full)) <= 1e-12
+
+
+@pytest.mark.parametrize("W", [0, 3])
+def test_prefix_rows_zero_query_give_prefix_mean_rest_unchanged(W):
+    # q = 0: every prefix row is the mean of v over [0, P); rows past the
+    # prefix are those of the plain causal / window mask.
+    S, d, P = 29, 8, 11
+    q = np.zeros((1, 2, S, d), np.float32)
+    k, v = _rand((1, 1, S, d)), _rand((1, 1, S, d))
+    out = oracle.prefill(q, k, v, causal=1, W=W, prefix=P)
+    mean = v[0, 0, :P].astype(np.float64).mean(0)
+    assert np.allclose(out[0, :, :P], mean, rtol=0, atol=1e-12)
+    q2 = _rand((1, 2, S, d))
+    a = oracle.prefill(q2, k, v, causal=1, W=W, prefix=P)
+    b = oracle.prefill(q2, k, v, causal=1, W=W)
+    assert np.array_equal(a[0, :, P:], b[0, :, P:])
+
+
+@pytest.mark.parametrize("S,P,W", [(9, 4, 0), (9, 4, 4), (7, 7, 0), (12, 5, 2)])
+def test_prefix_c_oracle_matches_python_twin(S, P, W):
+    q, k, v = _rand((1, 2, S, 6)), _rand((1, 1, S, 6)), _rand((1, 1, S, 6))
+    got = oracle.prefill(q, k, v, causal=1, W=W, prefix=P, m0=3)
+    ref = np.array(pyref.prefill(q.astype(float).tolist(), k.astype(float).tolist(),
+                                 v.astype(float).tolist(), True, W, 3, P=P))
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_prefix_needs_the_causal_mask():
+    q, k, v = _rand((1, 1, 4, 4)), _rand((1, 1, 4, 4)), _rand((1, 1, 4, 4))
+    with pytest.raises(ValueError):
+        oracle.prefill(q, k, v, causal=0, prefix=2)
+    with pytest.raises(ValueError):
+        oracle.prefill(q, k, v, causal=1, prefix=-1)
