@@ -15,7 +15,8 @@ import torch
 
 # The workloads: name -> sizes. Symbols follow the pages' notation table
 # (Part 1, §1): B batch, S sequence, H_q / H_kv query / KV heads, d_h head
-# size, W window (0 = none), m0 position of row 0, base the RoPE base.
+# size, W window (0 = none), prefix P of the bidirectional prefix (absent = 0),
+# m0 position of row 0, base the RoPE base.
 WORKLOADS = {
     "tiny_prefill_f32": dict(kind="prefill", B=1, S=128, Hq=4, Hkv=2, d=64, causal=1, W=0,
                              m0=0, base=10000.0, dtype="f32", seed=1),
@@ -26,6 +27,12 @@ WORKLOADS = {
                                         seed=3),
     "local_prefill_s65536_w512": dict(kind="prefill", B=1, S=65536, Hq=64, Hkv=8, d=128,
                                       causal=1, W=512, m0=0, base=10000.0, dtype="bf16", seed=4),
+    # prefix-bidirectional regime (Part 2, §11.1): rows < prefix see the whole prefix
+    "prefix_prefill_s2048_p512": dict(kind="prefill", B=4, S=2048, Hq=32, Hkv=8, d=128, causal=1,
+                                      W=0, prefix=512, m0=0, base=10000.0, dtype="bf16", seed=6),
+    "prefix_local_prefill_s16384_w4096_p1024": dict(kind="prefill", B=2, S=16384, Hq=32, Hkv=8,
+                                                    d=128, causal=1, W=4096, prefix=1024, m0=0,
+                                                    base=10000.0, dtype="bf16", seed=7),
     "gqa_decode_sk32768": dict(kind="decode", B=64, Sk=32768, Hq=128, Hkv=8, d=128, W=0,
                                m=32767, base=10000.0, dtype="bf16", seed=5),
 }

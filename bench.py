@@ -31,7 +31,8 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 HEADLINE = "gqa_prefill_s2048"
 DECODE = "gqa_decode_sk32768"
-OTHERS = ("window_prefill_s16384_w4096", "local_prefill_s65536_w512")
+OTHERS = ("window_prefill_s16384_w4096", "local_prefill_s65536_w512",
+          "prefix_prefill_s2048_p512", "prefix_local_prefill_s16384_w4096_p1024")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_gqa_s2048_traffic.json")
 PREFILL_SOURCES = ("transformer_attention_amd/csrc/prefill_kernel.hpp",
                    "transformer_attention_amd/csrc/device_common.hpp")
@@ -41,19 +42,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def n_visible(S, causal, W):
+def n_visible(S, causal, W, P=0):
     """Visible (query, key) pairs of one (b, h): key j visible to query i iff
-    j <= i and, with a window, i - j < W (Part 2, §10.2)."""
+    j <= i and, with a window, i - j < W (Part 2, §10.2); with a prefix of P
+    positions, rows i < P see exactly the keys j < P (Part 2, §11.1)."""
     if not causal:
         return S * S
+    P = min(P, S)
     if W == 0 or W >= S:
-        return S * (S + 1) // 2
-    # rows i < W see i + 1 keys, the rest see W keys
-    return W * (W + 1) // 2 + (S - W) * W
+        rest = S * (S + 1) // 2 - P * (P + 1) // 2     # rows P .. S-1 see i + 1 keys
+    else:
+        def upto(n):  # sum over rows i < n of min(i + 1, W)
+            m = min(n, W)
+            return m * (m + 1) // 2 + max(0, n - W) * W
+        rest = upto(S) - upto(P)
+    return P * P + rest
 
 
 def prefill_flops(w):
-    return 4 * w["B"] * w["Hq"] * w["d"] * n_visible(w["S"], w["causal"], w["W"])
+    return 4 * w["B"] * w["Hq"] * w["d"] * n_visible(w["S"], w["causal"], w["W"],
+                                                     w.get("prefix", 0))
 
 
 def prefill_bytes(w):
@@ -95,7 +103,7 @@ def time_prefill(taa, torch, name, steps, warmup):
     w = apex_inputs.WORKLOADS[name]
     q, k, v = apex_inputs.workload_inputs(name, device="cuda")
     kr, o = torch.empty_like(k), torch.empty_like(q)
-    kw = dict(causal=w["causal"], W=w["W"], m0=w["m0"], base=w["base"])
+    kw = dict(causal=w["causal"], W=w["W"], m0=w["m0"], base=w["base"], prefix=w.get("prefix", 0))
 
     def step(ev=None):
         if ev:

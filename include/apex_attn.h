@@ -71,14 +71,18 @@ int apex_rope_qk(const void* q, const void* k, void* q_out, void* k_out, int B, 
 
 /*
  * apex_attn_prefill -- o = softmax(RoPE(q) RoPE(k)^T / sqrt(d_h)) v with GQA
- * and the causal / window mask (Part 2, §6.2, §8.2, §10.2).
+ * and the causal / window / prefix-bidirectional masks (Part 2, §6.2, §8.2,
+ * §10.2, §11.1).
  *   q: [B, H_q, S, d_h]   (read only)
  *   k: [B, H_kv, S, d_h]  (read only)
  *   v: [B, H_kv, S, d_h]  (read only)
  *   o: [B, H_q, S, d_h]   output; must not overlap any input.
  *   causal: 1 = key j visible to query i only if j <= i; 0 = all visible.
  *   W: window width (> 0 requires causal = 1); 0 = no window.
- *   m0: position of row 0 (>= 0). The mask depends on i - j only.
+ *   prefix: P >= 0 (> 0 requires causal = 1). Rows i < P form the
+ *     bidirectional prefix: each sees exactly the keys j < P. Rows i >= P keep
+ *     the causal mask and the window. 0 = no prefix.
+ *   m0: position of row 0 (>= 0). The mask depends on row indices only.
  *   apply_rope:
  *     1 = q and k are raw: k is rotated once into k_rope_out (one elementwise
  *         launch), then the attention launch rotates q while its tiles load
@@ -91,14 +95,14 @@ int apex_rope_qk(const void* q, const void* k, void* q_out, void* k_out, int B, 
  *     values a KV cache stores). It may equal k (in-place rotation) but must
  *     not overlap q, v or o.
  * Errors: APEX_EINVAL for H_q % H_kv != 0, sizes < 1, W < 0, W > 0 with
- * causal = 0, m0 < 0, apply_rope not 0/1/2, base <= 0 with apply_rope, a
- * NULL required pointer, an unknown dtype; APEX_EUNSUPPORTED for d_h not 64
- * or 128.
+ * causal = 0, prefix < 0, prefix > 0 with causal = 0, m0 < 0, apply_rope not
+ * 0/1/2, base <= 0 with apply_rope, a NULL required pointer, an unknown
+ * dtype; APEX_EUNSUPPORTED for d_h not 64 or 128.
  */
 int apex_attn_prefill(const void* q, const void* k, const void* v, void* o,
                       void* k_rope_out, int B, int S, int H_q, int H_kv, int d_h,
-                      int causal, int W, int64_t m0, double base, int apply_rope,
-                      int dtype, void* stream);
+                      int causal, int W, int prefix, int64_t m0, double base,
+                      int apply_rope, int dtype, void* stream);
 
 /*
  * apex_attn_decode_workspace_bytes -- bytes of scratch apex_attn_decode needs

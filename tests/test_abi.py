@@ -71,10 +71,10 @@ def test_rope_rejects(L):
     assert _rope(L, q=None, qo=None, Hq=0, d=96) == EUNSUP
 
 
-def _prefill(L, q=P, k=P, v=P, o=P, kr=P, B=1, S=8, Hq=4, Hkv=2, d=128, causal=1, W=0, m0=0,
-             base=1e4, rope=1, dtype=1):
-    return L.apex_attn_prefill(q, k, v, o, kr, B, S, Hq, Hkv, d, causal, W, m0, base, rope, dtype,
-                               None)
+def _prefill(L, q=P, k=P, v=P, o=P, kr=P, B=1, S=8, Hq=4, Hkv=2, d=128, causal=1, W=0, prefix=0,
+             m0=0, base=1e4, rope=1, dtype=1):
+    return L.apex_attn_prefill(q, k, v, o, kr, B, S, Hq, Hkv, d, causal, W, prefix, m0, base, rope,
+                               dtype, None)
 
 
 def test_prefill_rejects(L):
@@ -86,6 +86,8 @@ def test_prefill_rejects(L):
     assert _prefill(L, Hkv=0) == EINVAL
     assert _prefill(L, W=-1) == EINVAL
     assert _prefill(L, causal=0, W=4) == EINVAL     # a window needs the causal mask
+    assert _prefill(L, prefix=-1) == EINVAL
+    assert _prefill(L, causal=0, prefix=3) == EINVAL  # so does a bidirectional prefix
     assert _prefill(L, causal=2) == EINVAL
     assert _prefill(L, m0=-3) == EINVAL
     assert _prefill(L, base=0.0) == EINVAL

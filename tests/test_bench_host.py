@@ -18,6 +18,14 @@ def test_n_visible_matches_the_mask(S, W, causal):
     assert bench.n_visible(S, causal, W) == brute
 
 
+@pytest.mark.parametrize("S", [1, 7, 64, 100])
+@pytest.mark.parametrize("W", [0, 1, 3, 64])
+@pytest.mark.parametrize("P", [1, 5, 63, 100, 150])
+def test_n_visible_with_prefix_matches_the_mask(S, W, P):
+    brute = sum(oracle.visible(i, j, 1, W, P) for i in range(S) for j in range(S))
+    assert bench.n_visible(S, 1, W, P) == brute
+
+
 def test_workload_counts():
     import apex_inputs
     w = apex_inputs.WORKLOADS

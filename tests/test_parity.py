@@ -50,7 +50,8 @@ def _check(got, ref, dtype, what):
 
 def _rows(B, Hq, S, n_random, seed):
     rng = np.random.default_rng(seed)
-    iset = [i for i in (0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 255, 256, 511, 512, 513,
+    iset = [i for i in (0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 255, 256, 511, 512, 513, 1023,
+                        1024, 1025,
                         S // 2, S - 65, S - 64, S - 33, S - 32, S - 2, S - 1) if 0 <= i < S]
     rows = set()
     for b in sorted({0, B - 1}):
@@ -121,6 +122,33 @@ def test_prefill_small(taa, case):
     _check(o, ref, dtype, "prefill %s" % (case,))
 
 
+PREFIX_CASES = [
+    # B, S, Hq, Hkv, d, W, prefix, dtype -- prefix-bidirectional regime
+    (1, 100, 4, 2, 128, 0, 37, "bf16"),
+    (1, 300, 8, 2, 128, 0, 129, "bf16"),     # the prefix ends inside a key tile
+    (1, 300, 8, 8, 64, 0, 300, "bf16"),      # all prefix: bidirectional attention
+    (2, 513, 16, 4, 128, 64, 200, "bf16"),   # window after the prefix, ragged tail
+    (1, 257, 4, 1, 128, 16, 1, "bf16"),      # P = 1: the causal mask
+    (1, 1000, 32, 8, 128, 300, 520, "bf16"),
+    (1, 640, 64, 8, 128, 128, 64, "bf16"),
+    (1, 130, 4, 2, 64, 0, 45, "f32"),
+    (1, 77, 4, 1, 128, 9, 20, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", PREFIX_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_prefix(taa, case):
+    B, S, Hq, Hkv, d, W, P, dtype = case
+    _say("prefill prefix", case)
+    q, k, v = apex_inputs.prefill_inputs(B, S, Hq, Hkv, d, dtype, seed=S + P, device="cuda")
+    o = torch.empty_like(q)
+    kr = torch.empty_like(k)
+    taa.apex_attn_prefill(q, k, v, o, kr, causal=1, W=W, prefix=P, apply_rope=1)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), causal=1, W=W, prefix=P)
+    _check(o, ref, dtype, "prefill prefix %s" % (case,))
+
+
 def test_k_rope_out_holds_rotated_keys_and_may_alias_k(taa):
     B, S, Hq, Hkv, d = 1, 200, 8, 2, 128
     q, k, v = apex_inputs.prefill_inputs(B, S, Hq, Hkv, d, "bf16", seed=5, device="cuda")
@@ -158,17 +186,18 @@ def _run_prefill_workload(taa, name, n_random):
     _say("workload", name, w)
     q, k, v = apex_inputs.workload_inputs(name, device="cuda")
     o, kr = torch.empty_like(q), torch.empty_like(k)
+    P = w.get("prefix", 0)
     taa.apex_attn_prefill(q, k, v, o, kr, causal=w["causal"], W=w["W"], m0=w["m0"],
-                          base=w["base"], apply_rope=1)
+                          base=w["base"], apply_rope=1, prefix=P)
     torch.cuda.synchronize()
     B, Hq, S, d = q.shape
     if n_random is None:
         ref = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), causal=w["causal"], W=w["W"],
-                             m0=w["m0"], base=w["base"])
+                             m0=w["m0"], base=w["base"], prefix=P)
         return _check(o, ref, w["dtype"], name)
     rows = _rows(B, Hq, S, n_random, seed=w["seed"])
     ref = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), causal=w["causal"], W=w["W"], m0=w["m0"],
-                         base=w["base"], rows=rows)
+                         base=w["base"], rows=rows, prefix=P)
     got = o.reshape(-1, d)[torch.from_numpy(rows).to(o.device)]
     return _check(got, ref, w["dtype"], "%s (%d sampled rows)" % (name, rows.size))
 
@@ -187,6 +216,14 @@ def test_workload_window_prefill_s16384_w4096(taa):
 
 def test_workload_local_prefill_s65536_w512(taa):
     _run_prefill_workload(taa, "local_prefill_s65536_w512", 3000)
+
+
+def test_workload_prefix_prefill_s2048_p512(taa):
+    _run_prefill_workload(taa, "prefix_prefill_s2048_p512", 3000)
+
+
+def test_workload_prefix_local_prefill_s16384_w4096_p1024(taa):
+    _run_prefill_workload(taa, "prefix_local_prefill_s16384_w4096_p1024", 1500)
 
 
 # --------------------------------------------------------------- decode ----

@@ -37,8 +37,8 @@ def lib():
                                  ctypes.c_size_t)
         L.apex_rope_qk.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, dbl, i32, vp]
         L.apex_rope_qk.restype = i32
-        L.apex_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64,
-                                        dbl, i32, i32, vp]
+        L.apex_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                        i64, dbl, i32, i32, vp]
         L.apex_attn_prefill.restype = i32
         L.apex_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.apex_attn_decode_workspace_bytes.restype = sz
@@ -101,14 +101,15 @@ def apex_rope_qk(q, k, q_out=None, k_out=None, m0=0, base=10000.0, stream=None):
 
 
 def apex_attn_prefill(q, k, v, o, k_rope_out=None, causal=1, W=0, m0=0, base=10000.0,
-                      apply_rope=1, stream=None):
+                      apply_rope=1, stream=None, prefix=0):
     """o = softmax(RoPE(q) RoPE(k)^T / sqrt(d_h)) v. apply_rope: 1 = rotate q and k
-    (RoPE(k) lands in k_rope_out), 2 = rotate q only (k holds rotated keys), 0 = none."""
+    (RoPE(k) lands in k_rope_out), 2 = rotate q only (k holds rotated keys), 0 = none.
+    prefix: rows i < prefix see exactly the keys j < prefix (bidirectional prefix)."""
     B, Hq, S, d = q.shape
     Hkv = k.shape[1]
     _check("apex_attn_prefill",
            lib().apex_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(k_rope_out), B, S, Hq,
-                                   Hkv, d, int(causal), int(W), int(m0), float(base),
+                                   Hkv, d, int(causal), int(W), int(prefix), int(m0), float(base),
                                    int(apply_rope), _dtype_code(q), _stream(q, stream)))
 
 

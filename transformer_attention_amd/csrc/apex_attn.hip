@@ -94,11 +94,12 @@ int apex_rope_qk(const void* q, const void* k, void* q_out, void* k_out, int B, 
 }
 
 int apex_attn_prefill(const void* q, const void* k, const void* v, void* o, void* k_rope_out,
-                      int B, int S, int H_q, int H_kv, int d_h, int causal, int W, int64_t m0,
-                      double base, int apply_rope, int dtype, void* stream) {
+                      int B, int S, int H_q, int H_kv, int d_h, int causal, int W, int prefix,
+                      int64_t m0, double base, int apply_rope, int dtype, void* stream) {
   if (!q || !k || !v || !o || (apply_rope == 1 && !k_rope_out)) return APEX_EINVAL;
   if (B < 1 || S < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0) return APEX_EINVAL;
   if (W < 0 || (W > 0 && !causal) || (causal != 0 && causal != 1)) return APEX_EINVAL;
+  if (prefix < 0 || (prefix > 0 && !causal)) return APEX_EINVAL;
   if (m0 < 0 || apply_rope < 0 || apply_rope > 2 || (apply_rope && !(base > 0.0)))
     return APEX_EINVAL;
   const int dc = check_dims(d_h, dtype);
@@ -120,7 +121,8 @@ int apex_attn_prefill(const void* q, const void* k, const void* v, void* o, void
     p.v = (const uint16_t*)v;
     p.o = (uint16_t*)o;
     p.S = S; p.Hq = H_q; p.Hkv = H_kv; p.G = G;
-    p.causal = causal; p.W = W; p.m0 = m0; p.base = base; p.apply_rope = apply_rope != 0;
+    p.causal = causal; p.W = W; p.P = prefix < S ? prefix : S;
+    p.m0 = m0; p.base = base; p.apply_rope = apply_rope != 0;
     p.g_pack = head_pack(G);
     p.bm = apex::kPfRows / p.g_pack;
     p.n_pos_tiles = (S + p.bm - 1) / p.bm;
@@ -142,7 +144,8 @@ int apex_attn_prefill(const void* q, const void* k, const void* v, void* o, void
     p.v = (const float*)v;
     p.o = (float*)o;
     p.S = S; p.Hq = H_q; p.Hkv = H_kv; p.G = G;
-    p.causal = causal; p.W = W; p.m0 = m0; p.base = base; p.apply_rope = apply_rope != 0;
+    p.causal = causal; p.W = W; p.P = prefix < S ? prefix : S;
+    p.m0 = m0; p.base = base; p.apply_rope = apply_rope != 0;
     p.scale = (float)(1.0 / sqrt((double)d_h));
     if (B > 65535 || H_q > 65535) return APEX_EUNSUPPORTED;
     const dim3 grid((S + apex::kF32Rows - 1) / apex::kF32Rows, H_q, B);

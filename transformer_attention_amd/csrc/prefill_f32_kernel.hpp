@@ -1,5 +1,5 @@
 // prefill_f32_kernel.hpp -- attention prefill with fp32 storage and fp32 math
-// (APEX-1 Mathematical Reference, Part 2, §6.2, §8.2, §10.2; Q rotated by
+// (APEX-1 Mathematical Reference, Part 2, §6.2, §8.2, §10.2, §11.1; Q rotated by
 // RoPE, Part 1, §4.2, as it loads).
 //
 // The fp32 workloads are small (correctness-sized), so this kernel is a plain
@@ -25,6 +25,7 @@ struct PrefillF32Params {
   float* o;
   int S, Hq, Hkv, G;
   int causal, W;
+  int P;              // prefix rows (bidirectional within [0, P)); <= S
   long long m0;
   double base;
   int apply_rope;
@@ -71,7 +72,8 @@ __global__ __launch_bounds__(kF32Threads) void prefill_f32_kernel(PrefillF32Para
   int j_lo = 0, j_hi = p.S - 1;
   if (p.causal) {
     j_hi = min(p.S - 1, r0 + kF32Rows - 1);
-    if (p.W > 0) j_lo = max(0, r0 - p.W + 1);
+    if (r0 < p.P) j_hi = max(j_hi, p.P - 1);             // prefix rows see the whole prefix
+    if (p.W > 0 && r0 >= p.P) j_lo = max(0, r0 - p.W + 1);
   }
   const float* kbase = p.k + ((size_t)b * p.Hkv + kvh) * p.S * D;
   const float* vbase = p.v + ((size_t)b * p.Hkv + kvh) * p.S * D;
@@ -96,7 +98,8 @@ __global__ __launch_bounds__(kF32Threads) void prefill_f32_kernel(PrefillF32Para
       dot += __shfl_xor(dot, 1, 64);
       const int j = j0 + jj;
       bool vis = j < p.S;
-      if (p.causal) vis = vis && j <= row && (p.W == 0 || row - j < p.W);
+      if (p.causal)
+        vis = vis && (row < p.P ? j < p.P : (j <= row && (p.W == 0 || row - j < p.W)));
       sc[jj] = vis ? dot * p.scale : kNegInf;
       mx = fmaxf(mx, sc[jj]);
     }

@@ -1,7 +1,8 @@
 // prefill_kernel.hpp -- flash-style attention prefill for gfx950 in bf16:
 //   O = softmax(Q K^T / sqrt(d_h)) V with GQA, causal and window masks
 // (APEX-1 Mathematical Reference, Part 2, §6.2 "Formula", §8.2 GQA head map,
-// §10.2 window mask), Q rotated by RoPE (Part 1, §4.2) as its tile loads.
+// §10.2 window mask, §11.1 prefix-bidirectional regime), Q rotated by RoPE
+// (Part 1, §4.2) as its tile loads.
 //
 // Work decomposition
 //   One workgroup = 4 waves = 128 query rows that all read the same KV head:
@@ -58,6 +59,7 @@ struct PrefillParams {
   uint16_t* o;
   int S, Hq, Hkv, G;
   int causal, W;
+  int P;              // prefix rows (bidirectional within [0, P)); <= S
   long long m0;
   double base;
   int apply_rope;     // rotate q while it loads
@@ -77,11 +79,16 @@ __device__ __forceinline__ int swz(int r) {
 }
 
 // True when every key of [j0, j0 + kPfBN) is visible to every row of
-// [r0, r0 + 32) (Part 2, §10.2), so the tile needs no mask.
+// [r0, r0 + 32) (Part 2, §10.2, §11.1), so the tile needs no mask: it lies
+// below the smallest last-visible key of the rows (P - 1 for prefix rows, the
+// row itself otherwise) and at or above the largest first-visible key (0 for
+// prefix rows, row - W + 1 in a window).
 // Bitwise, not short-circuit, so that it adds no branch to the loop body.
-__device__ __forceinline__ bool tile_is_full(int j0, int r0, int S, int causal, int W) {
+__device__ __forceinline__ bool tile_is_full(int j0, int r0, int S, int causal, int W, int P) {
   const int j1 = j0 + kPfBN - 1;
-  return (j1 < S) & ((causal == 0) | ((j1 <= r0) & ((W == 0) | (j0 >= r0 + 32 - W))));
+  const int min_hi = r0 < P ? P - 1 : r0;
+  const int max_lo = (W > 0) & (r0 + 31 >= P) ? r0 + 32 - W : 0;
+  return (j1 < S) & ((causal == 0) | ((j1 <= min_hi) & (j0 >= max_lo)));
 }
 
 template <int D>
@@ -122,7 +129,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
   int j_lo = 0, j_hi = p.S - 1;
   if (p.causal) {
     j_hi = min(p.S - 1, p0 + p.bm - 1);
-    if (p.W > 0) j_lo = max(0, p0 - p.W + 1);
+    if (p0 < p.P) j_hi = max(j_hi, p.P - 1);               // prefix rows see the whole prefix
+    if (p.W > 0 && p0 >= p.P) j_lo = max(0, p0 - p.W + 1);
   }
   const int t_lo = j_lo / kPfBN, t_hi = j_hi / kPfBN;
 
@@ -214,8 +222,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
   };
 
   // visible keys of this lane's row: [vis_lo, vis_hi]
-  const int vis_hi = p.causal ? min(row, p.S - 1) : p.S - 1;
-  const int vis_lo = (p.causal && p.W > 0) ? row - p.W + 1 : 0;
+  const int vis_hi = !p.causal ? p.S - 1 : (row < p.P ? p.P - 1 : min(row, p.S - 1));
+  const int vis_lo = (p.causal && p.W > 0 && row >= p.P) ? row - p.W + 1 : 0;
   const unsigned vis_span = (unsigned)(vis_hi - vis_lo);
 
   f32x16 oacc[DB];
@@ -225,7 +233,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
 
   f32x16 sa[2], sb[2];
   qk(kbuf[0], sa);
-  bool full_a = tile_is_full(t_lo * kPfBN, pw, p.S, p.causal, p.W), full_b = true;
+  bool full_a = tile_is_full(t_lo * kPfBN, pw, p.S, p.causal, p.W, p.P), full_b = true;
   __syncthreads();  // every wave is done with kbuf[0] before K(t_lo + 2) lands there
 
   // One 64-key tile: S(t+1) = K(t+1) Q^T is issued to the matrix cores while
@@ -263,7 +271,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
 
     // S(t+1): on the last tile this reads a stale buffer and is discarded
     qk(kbuf[(it + 1) & 1], s_next);
-    full_next = tile_is_full((t + 1) * kPfBN, pw, p.S, p.causal, p.W);
+    full_next = tile_is_full((t + 1) * kPfBN, pw, p.S, p.causal, p.W, p.P);
 
     float lsum = 0.0f;
     u32x4 pk[2][2];
