@@ -46,6 +46,7 @@ def lib():
         L.apex_oracle_visible.argtypes = [i64, i64, i32, i64, i64]
         L.apex_oracle_prefill.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                           i64, i64, dbl, i32, i64, vp, vp, vp, i32]
+        L.apex_oracle_rmsnorm.argtypes = [vp, vp, i32, i64, i32, dbl, vp, i32]
         L.apex_oracle_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                          i64, dbl, i32, i64, vp, vp, i32]
         _lib = L
@@ -168,3 +169,21 @@ def decode(q, k_cache, v_cache, k_new, v_new, m, W=0, base=10000.0, apply_rope=T
         raise ValueError("apex_oracle_decode rejected its arguments")
     return out.reshape(B, Hq, 1, d) if rows is None else out
 
+
+
+def rmsnorm(x, gamma, eps=1e-6, nthreads=None):
+    """RMSNorm over the last dimension: x [..., d], gamma [d] (float32, or bf16
+    bits / torch bf16, both the same dtype). Returns fp64 of x's shape."""
+    xa, dt = _as_input(x)
+    ga, dg = _as_input(gamma)
+    if dt != dg:
+        raise TypeError("x and gamma must share a dtype")
+    d = xa.shape[-1]
+    if ga.shape != (d,):
+        raise ValueError("gamma must have shape [d]")
+    rows = xa.size // d
+    out = np.empty(xa.shape, np.float64)
+    if lib().apex_oracle_rmsnorm(_ptr(xa), _ptr(ga), dt, rows, d, float(eps), _ptr(out),
+                                 nthreads or default_threads()) != 0:
+        raise ValueError("apex_oracle_rmsnorm rejected its arguments")
+    return out

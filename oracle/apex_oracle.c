@@ -18,6 +18,8 @@
  *   - GQA: G = H_q/H_kv, query head h reads KV head floor(h/G)  (Part 2, §8.2).
  *   - Window mask: key j is visible to query i iff 0 <= i-j < W and j <= i
  *     (Part 2, §10.2). W = 0 means no window. Non-causal: every key visible.
+ *   - RMSNorm (Part 1, §3.2): y = x / sqrt(mean(x^2) + eps) * gamma over each
+ *     row of d features.
  *   - Prefix-bidirectional regime (Part 2, §11.1, picture in §11.3): with a
  *     prefix of P positions, a query i < P sees exactly the keys j < P; the
  *     other queries keep the causal (and window) mask. P = 0: no prefix.
@@ -307,5 +309,40 @@ int apex_oracle_decode(const void* q, const void* k_cache, const void* v_cache,
   decode_ctx c = {q, k_cache, v_cache, k_new, v_new, dtype, Sk, Hq, Hkv, d, W, apply_rope,
                   m, base, rows, out};
   parallel_for(nrows, nthreads, decode_rows, &c);
+  return 0;
+}
+
+/* ----------------------------- RMSNorm ----------------------------- */
+typedef struct {
+  const void *x, *gamma;
+  int dtype, d;
+  double eps;
+  double* out;
+} rmsnorm_ctx;
+
+static void rmsnorm_rows(void* p, int64_t lo, int64_t hi) {
+  rmsnorm_ctx* c = (rmsnorm_ctx*)p;
+  for (int64_t r = lo; r < hi; r++) {
+    double msq = 0.0;
+    for (int t = 0; t < c->d; t++) {
+      double v = load_elem(c->x, c->dtype, r * c->d + t);
+      msq += v * v;
+    }
+    msq /= c->d;
+    double rms = sqrt(msq + c->eps);
+    for (int t = 0; t < c->d; t++)
+      c->out[r * c->d + t] =
+          load_elem(c->x, c->dtype, r * c->d + t) / rms * load_elem(c->gamma, c->dtype, t);
+  }
+}
+
+/* RMSNorm of `rows` rows of d features: x [rows, d], gamma [d] (fp32 or bf16
+ * bits), out [rows, d] doubles. Returns 0, or -1 on invalid arguments. */
+int apex_oracle_rmsnorm(const void* x, const void* gamma, int dtype, int64_t rows, int d,
+                        double eps, double* out, int nthreads) {
+  if (!x || !gamma || !out || rows < 1 || d < 1 || !(eps >= 0.0) || (dtype != 0 && dtype != 1))
+    return -1;
+  rmsnorm_ctx c = {x, gamma, dtype, d, eps, out};
+  parallel_for(rows, nthreads, rmsnorm_rows, &c);
   return 0;
 }

@@ -102,3 +102,12 @@ def decode(q, k_cache, v_cache, k_new, v_new, m, W=0, base=10000.0, apply_rope=T
             heads.append(sdpa_row(qi, keys, vals)[0])
         out.append(heads)
     return out
+
+
+def rmsnorm(x, gamma, eps=1e-6):
+    """x [rows][d], gamma [d] -> rows divided by sqrt(mean of squares + eps), times gamma."""
+    out = []
+    for row in x:
+        rms = math.sqrt(sum(v * v for v in row) / len(row) + eps)
+        out.append([v / rms * g for v, g in zip(row, gamma)])
+    return out

@@ -501,3 +501,65 @@ def test_prefix_needs_the_causal_mask():
         oracle.prefill(q, k, v, causal=0, prefix=2)
     with pytest.raises(ValueError):
         oracle.prefill(q, k, v, causal=1, prefix=-1)
+
+
+# --------------------------------------------------------------------------
+# RMSNorm (Part 1, §3)
+# --------------------------------------------------------------------------
+def test_rmsnorm_worked_example(golden_dir):
+    g = _golden(golden_dir, "rmsnorm_worked_example.json")
+    x = np.array([g["x"]], np.float32)
+    out = oracle.rmsnorm(x, np.array(g["gamma"], np.float32), eps=g["eps"])[0]
+    # the printed steps, to the printed precision
+    assert abs(float(np.mean(x.astype(np.float64) ** 2)) - g["mean_of_squares"]) == 0
+    assert abs(math.sqrt(g["mean_of_squares"] + g["eps"]) - g["rms_printed"]) < 5e-5
+    assert np.max(np.abs(out - np.array(g["output_printed"]))) < 5e-5
+    # and the exact value behind them
+    exact = np.array(g["x"]) / math.sqrt(1.875 + 1e-6)
+    assert np.max(np.abs(out - exact)) < 1e-15
+
+
+@pytest.mark.parametrize("d", [1, 4, 64, 7168])
+def test_rmsnorm_output_mean_square_closed_form(d):
+    # with gamma = 1, mean(y^2) = mean(x^2) / (mean(x^2) + eps): the page's
+    # "mean(output^2) ~ 1" check made exact
+    x = _rand((5, d))
+    for eps in (1e-6, 0.5):
+        y = oracle.rmsnorm(x, np.ones(d, np.float32), eps=eps)
+        msq = (x.astype(np.float64) ** 2).mean(-1)
+        assert np.allclose((y ** 2).mean(-1), msq / (msq + eps), rtol=1e-12, atol=0)
+
+
+def test_rmsnorm_scale_invariance_and_gamma():
+    x = _rand((7, 96))
+    g = _rand((96,))
+    y1 = oracle.rmsnorm(x, np.ones(96, np.float32), eps=0.0)
+    for c in (0.25, 4.0, 1024.0):  # powers of two: c * x is exact in fp32
+        yc = oracle.rmsnorm((x * c).astype(np.float32), np.ones(96, np.float32), eps=0.0)
+        assert np.max(np.abs(yc - y1)) <= 1e-12
+    yg = oracle.rmsnorm(x, g, eps=0.0)
+    assert np.max(np.abs(yg - y1 * g.astype(np.float64))) <= 1e-12
+
+
+def test_rmsnorm_zero_row_and_bf16_widening():
+    x = np.zeros((2, 16), np.float32)
+    assert np.array_equal(oracle.rmsnorm(x, np.ones(16, np.float32)), np.zeros((2, 16)))
+    t = torch.randn(3, 40).to(torch.bfloat16)
+    gt = torch.randn(40).to(torch.bfloat16)
+    a = oracle.rmsnorm(t, gt, eps=1e-6)
+    b = oracle.rmsnorm(t.float().numpy(), gt.float().numpy(), eps=1e-6)
+    assert np.array_equal(a, b)
+
+
+def test_rmsnorm_c_oracle_matches_python_twin():
+    x, g = _rand((6, 33)), _rand((33,))
+    got = oracle.rmsnorm(x, g, eps=1e-3)
+    ref = np.array(pyref.rmsnorm(x.astype(float).tolist(), g.astype(float).tolist(), 1e-3))
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_rmsnorm_rejects():
+    with pytest.raises(ValueError):
+        oracle.rmsnorm(_rand((2, 8)), _rand((7,)))
+    with pytest.raises(ValueError):
+        oracle.rmsnorm(_rand((2, 8)), _rand((8,)), eps=-1.0)
