@@ -33,6 +33,11 @@ WORKLOADS = {
     "prefix_local_prefill_s16384_w4096_p1024": dict(kind="prefill", B=2, S=16384, Hq=32, Hkv=8,
                                                     d=128, causal=1, W=4096, prefix=1024, m0=0,
                                                     base=10000.0, dtype="bf16", seed=7),
+    # RMSNorm over d_model features (Part 1, §3); the pages' widths run 512 .. 7168
+    "rmsnorm_b4_s2048_d7168": dict(kind="rmsnorm", B=4, S=2048, d=7168, eps=1e-6, dtype="bf16",
+                                   seed=8),
+    "rmsnorm_b64_s2048_d512": dict(kind="rmsnorm", B=64, S=2048, d=512, eps=1e-6, dtype="bf16",
+                                   seed=9),
     "gqa_decode_sk32768": dict(kind="decode", B=64, Sk=32768, Hq=128, Hkv=8, d=128, W=0,
                                m=32767, base=10000.0, dtype="bf16", seed=5),
 }
@@ -78,8 +83,19 @@ def decode_inputs(B, Sk, Hq, Hkv, d, dtype="bf16", seed=0, device="cpu"):
     return q, k_cache, v_cache, k_new, v_new
 
 
+def rmsnorm_inputs(B, S, d, dtype="bf16", seed=0, device="cpu"):
+    """(x [B,S,d] ~ N(0,1), gamma [d] ~ 1 + 0.1 N(0,1)): gamma away from its
+    initial all-ones value so that the scale is exercised."""
+    dt = TORCH_DTYPE[dtype] if isinstance(dtype, str) else dtype
+    x = normal((B, S, d), seed * 16 + 0, dt, device)
+    g = normal((d,), seed * 16 + 1, torch.float32, device, chunk_dim0=False)
+    return x, (1.0 + 0.1 * g).to(dt)
+
+
 def workload_inputs(name, device="cpu"):
     w = WORKLOADS[name]
+    if w["kind"] == "rmsnorm":
+        return rmsnorm_inputs(w["B"], w["S"], w["d"], w["dtype"], w["seed"], device)
     if w["kind"] == "prefill":
         return prefill_inputs(w["B"], w["S"], w["Hq"], w["Hkv"], w["d"], w["dtype"], w["seed"],
                               device)

@@ -31,6 +31,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 HEADLINE = "gqa_prefill_s2048"
 DECODE = "gqa_decode_sk32768"
+RMSNORMS = ("rmsnorm_b4_s2048_d7168", "rmsnorm_b64_s2048_d512")
 OTHERS = ("window_prefill_s16384_w4096", "local_prefill_s65536_w512",
           "prefix_prefill_s2048_p512", "prefix_local_prefill_s16384_w4096_p1024")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_gqa_s2048_traffic.json")
@@ -75,6 +76,12 @@ def decode_bytes(w):
     read, o written, the new key and value read."""
     B, Sk, Hq, Hkv, d = w["B"], w["Sk"], w["Hq"], w["Hkv"], w["d"]
     return 2 * (2 * B * Hkv * Sk * d + 2 * B * Hq * d + 2 * B * Hkv * d)
+
+
+def rmsnorm_bytes(w):
+    """Algorithmic bytes of one RMSNorm call: x read once, y written once, gamma read."""
+    e = 2 if w["dtype"] == "bf16" else 4
+    return e * w["d"] * (2 * w["B"] * w["S"] + 1)
 
 
 def sources_sha(paths):
@@ -129,6 +136,26 @@ def time_prefill(taa, torch, name, steps, warmup):
     attn_min = min(e[1].elapsed_time(e[2]) for e in evs)
     del q, k, v, kr, o
     return w, wall * 1e3, rope_ms, attn_ms, attn_min
+
+
+def time_rmsnorm(taa, torch, name, steps, warmup):
+    import apex_inputs
+    w = apex_inputs.WORKLOADS[name]
+    x, g = apex_inputs.workload_inputs(name, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(warmup):
+        taa.apex_rmsnorm(x, g, y, eps=w["eps"])
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        taa.apex_rmsnorm(x, g, y, eps=w["eps"])
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    del x, g, y
+    return w, sum(ms) / len(ms), ms[0]
 
 
 def time_decode(taa, torch, steps, warmup):
@@ -309,6 +336,18 @@ def main():
                             "frac_of_bf16_peak": round(of / (oms * 1e-3) / 1e12
                                                        / PEAK_BF16_TFLOPS, 4)}
         extra["other_workloads"] = others
+        torch.cuda.empty_cache()
+        norms = {}
+        for name in RMSNORMS:
+            log("timing %s" % name)
+            rw, rms_mean, rms_min = time_rmsnorm(taa, torch, name, max(10, args.steps), 3)
+            rb = rmsnorm_bytes(rw)
+            norms[name] = {"ms_per_call": round(rms_mean, 4), "ms_min": round(rms_min, 4),
+                           "algorithmic_bytes": rb,
+                           "gbs": round(rb / (rms_mean * 1e-3) / 1e9, 1),
+                           "frac_of_hbm_peak": round(rb / (rms_mean * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                                     4)}
+        extra["rmsnorm"] = norms
         torch.cuda.empty_cache()
 
     line = {

@@ -105,6 +105,21 @@ int apex_attn_prefill(const void* q, const void* k, const void* v, void* o,
                       int apply_rope, int dtype, void* stream);
 
 /*
+ * apex_rmsnorm -- y = x / sqrt(mean(x^2) + eps) * gamma over each row of d
+ * features (Part 1, §3.2; the norm in front of attention, §3.5).
+ *   x: [rows, d] row-major (read only unless y == x).
+ *   gamma: [d] scale.
+ *   y: [rows, d] output; may equal x (in place) but must not partly overlap it.
+ *   All three in `dtype`; bf16 is computed in fp32 and y rounded once.
+ *   eps: >= 0 and finite (1e-6 on the pages).
+ * Errors: APEX_EINVAL for a NULL pointer, rows or d < 1, eps < 0 or not
+ * finite, an unknown dtype; APEX_EUNSUPPORTED for d not a multiple of 8 or
+ * d > 8192.
+ */
+int apex_rmsnorm(const void* x, const void* gamma, void* y, int64_t rows, int d, double eps,
+                 int dtype, void* stream);
+
+/*
  * apex_attn_decode_workspace_bytes -- bytes of scratch apex_attn_decode needs
  * for these sizes (the split-K partial results: per query head and split, a
  * running max, a sum and d_h fp32 accumulators). Returns 0 for invalid sizes.

@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["apex_attn_decode", "apex_attn_decode_workspace_bytes",
-                                    "apex_attn_prefill", "apex_rope_qk", "apex_strerror"]
+                                    "apex_attn_prefill", "apex_rmsnorm", "apex_rope_qk",
+                                    "apex_strerror"]
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -145,6 +146,23 @@ def test_decode_rejects(L):
     assert _decode(L, dtype=0) == EUNSUP    # decode is built for bf16 caches
     assert _decode(L, ws=None) == EWS
     assert _decode(L, wsb=16) == EWS
+
+
+def _rms(L, x=P, g=P, y=P, rows=4, d=64, eps=1e-6, dtype=1):
+    return L.apex_rmsnorm(x, g, y, rows, d, eps, dtype, None)
+
+
+def test_rmsnorm_rejects(L):
+    for kw in (dict(x=None), dict(g=None), dict(y=None)):
+        assert _rms(L, **kw) == EINVAL, kw
+    assert _rms(L, rows=0) == EINVAL
+    assert _rms(L, d=0) == EINVAL
+    assert _rms(L, eps=-1e-6) == EINVAL
+    assert _rms(L, eps=float("inf")) == EINVAL
+    assert _rms(L, eps=float("nan")) == EINVAL
+    assert _rms(L, dtype=3) == EINVAL
+    assert _rms(L, d=12) == EUNSUP      # not a multiple of 8
+    assert _rms(L, d=8200) == EUNSUP    # wider than the kernels hold in registers
 
 
 def test_binding_refuses_cpu_tensors():

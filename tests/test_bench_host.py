@@ -34,6 +34,7 @@ def test_workload_counts():
     assert bench.n_visible(65536, 1, 512) == 33423616
     assert bench.prefill_flops(w["gqa_prefill_s2048"]) == 137506062336
     assert bench.decode_bytes(w["gqa_decode_sk32768"]) == 8594391040
+    assert bench.rmsnorm_bytes(w["rmsnorm_b4_s2048_d7168"]) == 2 * 7168 * (2 * 4 * 2048 + 1)
 
 
 def test_multi_gpu_request_is_refused():

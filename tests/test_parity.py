@@ -323,3 +323,66 @@ def test_workload_gqa_decode_sk32768(taa):
         ref = oracle.decode(q[b:b + 1].cpu(), kcb[None], vcb[None], kn[b:b + 1].cpu(),
                             vn[b:b + 1].cpu(), m=w["m"], W=w["W"], base=w["base"])
         _check(o[b:b + 1], ref, "bf16", "%s batch %d (all %d heads)" % (name, b, Hq))
+
+
+# -------------------------------------------------------------- RMSNorm ----
+def _check_rmsnorm(got, ref, dtype, what):
+    got = got.detach().to("cpu", torch.float64).numpy().reshape(ref.shape)
+    err = np.abs(got - ref)
+    if dtype == "bf16":
+        # one rounding of y to bf16 (relative 2^-9) on top of fp32 arithmetic
+        bound = np.abs(ref) * 2.0 ** -8 + 1e-30
+        mean_rel = float(err.sum() / max(np.abs(ref).sum(), 1e-30))
+        _say("%s: max rel %.3g mean rel %.3g" % (what, float((err / (np.abs(ref) + 1e-30)).max()),
+                                                 mean_rel))
+        assert mean_rel <= 2.0 ** -9, (what, mean_rel)  # rounding alone averages ~2^-10
+    else:
+        bound = np.abs(ref) * 2e-6 + 1e-6
+        _say("%s: max abs %.3g" % (what, float(err.max())))
+    assert np.all(np.isfinite(got)), what
+    assert np.all(err <= bound), (what, float((err - bound).max()))
+
+
+RMSNORM_CASES = [
+    # rows, d, dtype, eps, in_place
+    (1, 8, "bf16", 1e-6, False),
+    (3, 520, "bf16", 1e-6, False),     # chunks not a multiple of the wave
+    (257, 4096, "bf16", 1e-6, True),
+    (100, 7168, "bf16", 1e-6, False),
+    (5, 8192, "bf16", 0.0, False),
+    (20000, 64, "bf16", 1e-6, False),  # more rows than resident waves: grid-stride
+    (64, 512, "f32", 1e-6, False),
+    (33, 1000, "f32", 0.25, True),
+    (7, 8192, "f32", 1e-6, False),
+]
+
+
+@pytest.mark.parametrize("case", RMSNORM_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_rmsnorm(taa, case):
+    rows, d, dtype, eps, in_place = case
+    _say("rmsnorm", case)
+    x, g = apex_inputs.rmsnorm_inputs(1, rows, d, dtype, seed=rows + d, device="cuda")
+    x0 = x.cpu()
+    y = taa.apex_rmsnorm(x, g, x if in_place else None, eps=eps)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm(x0, g.cpu(), eps=eps)
+    _check_rmsnorm(y, ref, dtype, "rmsnorm %s" % (case,))
+
+
+def test_rmsnorm_zero_rows_with_eps(taa):
+    x = torch.zeros(4, 256, dtype=torch.bfloat16, device="cuda")
+    g = torch.ones(256, dtype=torch.bfloat16, device="cuda")
+    y = taa.apex_rmsnorm(x, g, eps=1e-6)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y).item() == 0
+
+
+@pytest.mark.parametrize("name", ["rmsnorm_b4_s2048_d7168", "rmsnorm_b64_s2048_d512"])
+def test_workload_rmsnorm(taa, name):
+    w = apex_inputs.WORKLOADS[name]
+    _say("workload", name, w)
+    x, g = apex_inputs.workload_inputs(name, device="cuda")
+    y = taa.apex_rmsnorm(x, g, eps=w["eps"])
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm(x.cpu(), g.cpu(), eps=w["eps"])
+    _check_rmsnorm(y, ref, w["dtype"], name)

@@ -40,6 +40,8 @@ def lib():
         L.apex_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                         i64, dbl, i32, i32, vp]
         L.apex_attn_prefill.restype = i32
+        L.apex_rmsnorm.argtypes = [vp, vp, vp, i64, i32, dbl, i32, vp]
+        L.apex_rmsnorm.restype = i32
         L.apex_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.apex_attn_decode_workspace_bytes.restype = sz
         L.apex_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
@@ -111,6 +113,19 @@ def apex_attn_prefill(q, k, v, o, k_rope_out=None, causal=1, W=0, m0=0, base=100
            lib().apex_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(k_rope_out), B, S, Hq,
                                    Hkv, d, int(causal), int(W), int(prefix), int(m0), float(base),
                                    int(apply_rope), _dtype_code(q), _stream(q, stream)))
+
+
+def apex_rmsnorm(x, gamma, y=None, eps=1e-6, stream=None):
+    """y = x / sqrt(mean(x^2) + eps) * gamma over the last dimension of x
+    (y = a new tensor unless given; y may be x). Returns y."""
+    if y is None:
+        y = torch.empty_like(x)
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    _check("apex_rmsnorm",
+           lib().apex_rmsnorm(_ptr(x), _ptr(gamma), _ptr(y), rows, d, float(eps), _dtype_code(x),
+                              _stream(x, stream)))
+    return y
 
 
 def apex_attn_decode_workspace_bytes(B, H_q, H_kv, Sk, d_h):

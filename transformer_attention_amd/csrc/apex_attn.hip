@@ -10,6 +10,7 @@
 #include "decode_kernel.hpp"
 #include "prefill_f32_kernel.hpp"
 #include "prefill_kernel.hpp"
+#include "rmsnorm_kernel.hpp"
 #include "rope_kernel.hpp"
 
 namespace {
@@ -60,6 +61,22 @@ int decode_splits(int B, int Hkv, int n_hb, int Sk) {
   if (want > cap) want = cap;
   if (want < 1) want = 1;
   return (int)want;
+}
+
+template <typename T>
+int launch_rmsnorm(const apex::RmsNormParams& p, int nc, hipStream_t st) {
+  long long blocks = (p.rows + 3) / 4;
+  if (blocks > 4096) blocks = 4096;  // grid-stride beyond 16 workgroups per CU
+  const dim3 grid((unsigned)blocks), block(apex::kRmsThreads);
+  switch (nc) {
+    case 1: hipLaunchKernelGGL((apex::rmsnorm_kernel<T, 1>), grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((apex::rmsnorm_kernel<T, 2>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((apex::rmsnorm_kernel<T, 4>), grid, block, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((apex::rmsnorm_kernel<T, 8>), grid, block, 0, st, p); break;
+    case 16: hipLaunchKernelGGL((apex::rmsnorm_kernel<T, 16>), grid, block, 0, st, p); break;
+    default: return APEX_EUNSUPPORTED;
+  }
+  return launch_status();
 }
 
 }  // namespace
@@ -155,6 +172,20 @@ int apex_attn_prefill(const void* q, const void* k, const void* v, void* o, void
       hipLaunchKernelGGL(apex::prefill_f32_kernel<64>, grid, dim3(apex::kF32Threads), 0, st, p);
   }
   return launch_status();
+}
+
+int apex_rmsnorm(const void* x, const void* gamma, void* y, int64_t rows, int d, double eps,
+                 int dtype, void* stream) {
+  if (!x || !gamma || !y || rows < 1 || d < 1 || !(eps >= 0.0) || !(eps <= 1e30)) return APEX_EINVAL;
+  if (dtype != APEX_F32 && dtype != APEX_BF16) return APEX_EINVAL;
+  if (d % 8 != 0 || d > 8192) return APEX_EUNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  const int need = (d / 8 + 63) / 64;  // 16-byte chunks per lane
+  int nc = 1;
+  while (nc < need) nc *= 2;
+  apex::RmsNormParams p{x, gamma, y, (long long)rows, d, (float)eps};
+  return dtype == APEX_BF16 ? launch_rmsnorm<uint16_t>(p, nc, st) : launch_rmsnorm<float>(p, nc, st);
 }
 
 size_t apex_attn_decode_workspace_bytes(int B, int H_q, int H_kv, int Sk, int d_h) {
