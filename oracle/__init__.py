@@ -40,15 +40,19 @@ def lib():
         build(force=False)
         L = ctypes.CDLL(_LIB_PATH)
         i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
-        L.apex_oracle_theta.argtypes = [i32, dbl, vp]
-        L.apex_oracle_rope_row.argtypes = [vp, vp, i32, i64, dbl]
+        L.apex_oracle_theta.argtypes = [i32, dbl, dbl, vp]
+        L.apex_oracle_rope_row.argtypes = [vp, vp, i32, i64, dbl, dbl]
         L.apex_oracle_rope_row.restype = None
+        L.apex_oracle_yarn_theta.argtypes = [dbl, dbl]
+        L.apex_oracle_yarn_theta.restype = dbl
+        L.apex_oracle_yarn_attn_factor.argtypes = [dbl]
+        L.apex_oracle_yarn_attn_factor.restype = dbl
         L.apex_oracle_visible.argtypes = [i64, i64, i32, i64, i64]
         L.apex_oracle_prefill.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
-                                          i64, i64, dbl, i32, i64, vp, vp, vp, i32]
+                                          i64, i64, dbl, dbl, i32, i64, vp, vp, vp, i32]
         L.apex_oracle_rmsnorm.argtypes = [vp, vp, i32, i64, i32, dbl, vp, i32]
         L.apex_oracle_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
-                                         i64, dbl, i32, i64, vp, vp, i32]
+                                         i64, dbl, dbl, i32, i64, vp, vp, i32]
         _lib = L
     return _lib
 
@@ -88,17 +92,28 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
 
 
-def theta(d_h, base=10000.0):
+def theta(d_h, base=10000.0, yarn_s=1.0):
     out = np.empty(d_h // 2, np.float64)
-    if lib().apex_oracle_theta(d_h, base, _ptr(out)) != 0:
+    if lib().apex_oracle_theta(d_h, base, float(yarn_s), _ptr(out)) != 0:
         raise ValueError("bad theta arguments")
     return out
 
 
-def rope_row(x, pos, base=10000.0):
+def yarn_theta(theta_i, s):
+    """One RoPE frequency after YaRN at scale factor s (Part 1, §5.3-5.4)."""
+    return float(lib().apex_oracle_yarn_theta(float(theta_i), float(s)))
+
+
+def yarn_attn_factor(s):
+    """The YaRN attention temperature 0.1 ln(s) + 1 (Part 1, §5.5)."""
+    return float(lib().apex_oracle_yarn_attn_factor(float(s)))
+
+
+def rope_row(x, pos, base=10000.0, yarn_s=1.0):
     x = np.ascontiguousarray(x, np.float64)
     y = np.empty_like(x)
-    lib().apex_oracle_rope_row(_ptr(x), _ptr(y), x.shape[-1], int(pos), float(base))
+    lib().apex_oracle_rope_row(_ptr(x), _ptr(y), x.shape[-1], int(pos), float(base),
+                               float(yarn_s))
     return y
 
 
@@ -107,10 +122,11 @@ def visible(i, j, causal, W, prefix=0):
 
 
 def prefill(q, k, v, causal=True, W=0, m0=0, base=10000.0, apply_rope=True,
-            rows=None, probs=False, nthreads=None, prefix=0):
+            rows=None, probs=False, nthreads=None, prefix=0, yarn_s=1.0):
     """q [B,Hq,S,d]; k, v [B,Hkv,S,d] (float32, or bf16 bits as uint16 / torch bf16).
 
     prefix: P of the prefix-bidirectional regime (rows i < P see keys j < P).
+    yarn_s: YaRN scale factor (1 = plain RoPE and unscaled scores).
     rows: optional flat row indices (b*Hq+h)*S+i. Returns fp64 [len(rows), d]
     (or [B,Hq,S,d] when rows is None), and the [.., S] softmax weights if probs."""
     qa, dt = _as_input(q)
@@ -131,7 +147,7 @@ def prefill(q, k, v, causal=True, W=0, m0=0, base=10000.0, apply_rope=True,
     pr = np.empty((nrows, S), np.float64) if probs else None
     rc = lib().apex_oracle_prefill(_ptr(qa), _ptr(ka), _ptr(va), dt, B, S, Hq, Hkv, d,
                                    int(causal), int(W), int(prefix), int(m0), float(base),
-                                   int(apply_rope),
+                                   float(yarn_s), int(apply_rope),
                                    nrows, _ptr(rarr), _ptr(out), _ptr(pr),
                                    nthreads or default_threads())
     if rc != 0:
@@ -144,7 +160,7 @@ def prefill(q, k, v, causal=True, W=0, m0=0, base=10000.0, apply_rope=True,
 
 
 def decode(q, k_cache, v_cache, k_new, v_new, m, W=0, base=10000.0, apply_rope=True,
-           rows=None, nthreads=None):
+           rows=None, nthreads=None, yarn_s=1.0):
     """q [B,Hq,1,d] at position m; caches [B,Hkv,Sk,d]; k_new, v_new [B,Hkv,1,d] or None.
 
     rows: optional flat b*Hq+h. Returns fp64 [len(rows), d] or [B,Hq,1,d]."""
@@ -163,7 +179,7 @@ def decode(q, k_cache, v_cache, k_new, v_new, m, W=0, base=10000.0, apply_rope=T
     out = np.empty((nrows, d), np.float64)
     rc = lib().apex_oracle_decode(_ptr(qa), _ptr(kc), _ptr(vc), _ptr(kn), _ptr(vn), dt,
                                   B, Sk, Hq, Hkv, d, int(W), int(m), float(base),
-                                  int(apply_rope), nrows, _ptr(rarr), _ptr(out),
+                                  float(yarn_s), int(apply_rope), nrows, _ptr(rarr), _ptr(out),
                                   nthreads or default_threads())
     if rc != 0:
         raise ValueError("apex_oracle_decode rejected its arguments")

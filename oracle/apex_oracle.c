@@ -10,6 +10,10 @@
  * What it computes, and where that is defined (APEX-1 Mathematical Reference):
  *   - RoPE frequencies: theta_i = b^(-2i/d_h), i = 0 .. d_h/2-1
  *     (Part 1, §4.3 "Frequency Formula").
+ *   - YaRN (Part 1, §5.3-5.5), scale factor s >= 1 (1 = off): each frequency
+ *     is kept, divided by s, or divided by t s + (1 - t) by the regime of its
+ *     wavelength, and the attention scores are multiplied by
+ *     0.1 ln(s) + 1. beta_fast = 32, beta_slow = 1 (the pages' defaults).
  *   - RoPE rotation: the pair (x_2i, x_2i+1) is rotated by the angle m*theta_i,
  *     x'_2i = x_2i cos - x_2i+1 sin,  x'_2i+1 = x_2i sin + x_2i+1 cos
  *     (Part 1, §4.2 "Core Idea"; the sign and the adjacent pairing are fixed by
@@ -53,17 +57,42 @@ static double load_elem(const void* base, int dtype, int64_t idx) {
   return (double)f;
 }
 
-/* theta_i = b^(-2i/d_h)  (Part 1, §4.3). */
-int apex_oracle_theta(int d_h, double base, double* theta) {
-  if (d_h < 2 || (d_h & 1) || !(base > 0.0) || !theta) return -1;
-  for (int i = 0; i < d_h / 2; i++) theta[i] = pow(base, -2.0 * i / d_h);
+/* YaRN frequency (Part 1, §5.3 regimes, §5.4 interpolation) of one RoPE
+ * frequency at scale factor s, with beta_fast = 32 and beta_slow = 1. The
+ * regimes are taken in the table's order by the wavelength lambda = 2 pi /
+ * theta: lambda < beta_fast keeps theta; lambda > beta_slow * s divides it
+ * by s; otherwise theta / (t s + 1 - t) with t = (lambda / beta_slow - 1) /
+ * (s - 1) clamped to [0, 1] (the worked example of §5.6 clamps t). */
+#define ORACLE_TWO_PI 6.283185307179586476925286766559
+double apex_oracle_yarn_theta(double theta, double s) {
+  const double beta_fast = 32.0, beta_slow = 1.0;
+  if (s == 1.0) return theta;
+  const double lambda = ORACLE_TWO_PI / theta;
+  if (lambda < beta_fast) return theta;
+  if (lambda > beta_slow * s) return theta / s;
+  double t = (lambda / beta_slow - 1.0) / (s - 1.0);
+  if (t < 0.0) t = 0.0;
+  if (t > 1.0) t = 1.0;
+  return theta / (t * s + (1.0 - t));
+}
+
+/* The YaRN attention temperature: scores are multiplied by 0.1 ln(s) + 1
+ * (Part 1, §5.5). */
+double apex_oracle_yarn_attn_factor(double s) { return 0.1 * log(s) + 1.0; }
+
+/* theta_i = b^(-2i/d_h)  (Part 1, §4.3), then YaRN at scale s (s = 1: none). */
+int apex_oracle_theta(int d_h, double base, double yarn_s, double* theta) {
+  if (d_h < 2 || (d_h & 1) || !(base > 0.0) || !(yarn_s >= 1.0) || !theta) return -1;
+  for (int i = 0; i < d_h / 2; i++)
+    theta[i] = apex_oracle_yarn_theta(pow(base, -2.0 * i / d_h), yarn_s);
   return 0;
 }
 
 /* Rotate one row x[0..d_h) at position pos into y (y may equal x)  (Part 1, §4.2). */
-void apex_oracle_rope_row(const double* x, double* y, int d_h, int64_t pos, double base) {
+void apex_oracle_rope_row(const double* x, double* y, int d_h, int64_t pos, double base,
+                          double yarn_s) {
   for (int i = 0; i < d_h / 2; i++) {
-    double theta = pow(base, -2.0 * i / d_h);
+    double theta = apex_oracle_yarn_theta(pow(base, -2.0 * i / d_h), yarn_s);
     double angle = (double)pos * theta;
     double c = cos(angle), s = sin(angle);
     double a = x[2 * i], b = x[2 * i + 1];
@@ -134,7 +163,7 @@ typedef struct {
   const void *q, *k, *v;
   int dtype, S, Hq, Hkv, d, causal, W, apply_rope;
   int64_t P, m0;
-  double base;
+  double base, yarn_s;
   int b, kvh;
   double *krot, *vd;          /* [S, d] rotated keys and widened values of the group */
   const int64_t* rows;        /* requested flat rows of this group */
@@ -153,7 +182,7 @@ static void prefill_prepare_keys(void* p, int64_t lo, int64_t hi) {
       kr[t] = load_elem(c->k, c->dtype, (kv_off + j) * c->d + t);
       vr[t] = load_elem(c->v, c->dtype, (kv_off + j) * c->d + t);
     }
-    if (c->apply_rope) apex_oracle_rope_row(kr, kr, c->d, c->m0 + j, c->base);
+    if (c->apply_rope) apex_oracle_rope_row(kr, kr, c->d, c->m0 + j, c->base, c->yarn_s);
   }
 }
 
@@ -165,12 +194,12 @@ static void prefill_rows(void* p, int64_t lo, int64_t hi) {
   const double** vals = (const double**)malloc(sizeof(double*) * c->S);
   int64_t* idx = (int64_t*)malloc(sizeof(int64_t) * c->S);
   double* pr = (double*)malloc(sizeof(double) * c->S);
-  double scale = 1.0 / sqrt((double)c->d);
+  double scale = apex_oracle_yarn_attn_factor(c->yarn_s) / sqrt((double)c->d);
   for (int64_t r = lo; r < hi; r++) {
     int64_t flat = c->rows[r];                 /* (b*Hq + h)*S + i */
     int64_t i = flat % c->S;
     for (int t = 0; t < c->d; t++) q[t] = load_elem(c->q, c->dtype, flat * c->d + t);
-    if (c->apply_rope) apex_oracle_rope_row(q, q, c->d, c->m0 + i, c->base);
+    if (c->apply_rope) apex_oracle_rope_row(q, q, c->d, c->m0 + i, c->base, c->yarn_s);
     int64_t n = 0;
     for (int64_t j = 0; j < c->S; j++) {
       if (!apex_oracle_visible(i, j, c->causal, c->W, c->P)) continue;
@@ -198,12 +227,12 @@ static void prefill_rows(void* p, int64_t lo, int64_t hi) {
  * Returns 0, or -1 on invalid arguments. */
 int apex_oracle_prefill(const void* q, const void* k, const void* v, int dtype,
                         int B, int S, int Hq, int Hkv, int d, int causal, int W,
-                        int64_t P, int64_t m0, double base, int apply_rope,
+                        int64_t P, int64_t m0, double base, double yarn_s, int apply_rope,
                         int64_t nrows, const int64_t* rows, double* out, double* probs,
                         int nthreads) {
   if (!q || !k || !v || !out || B < 1 || S < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv ||
       d < 2 || (d & 1) || W < 0 || (W > 0 && !causal) || P < 0 || (P > 0 && !causal) ||
-      (dtype != 0 && dtype != 1) || (apply_rope && !(base > 0.0)))
+      (dtype != 0 && dtype != 1) || (apply_rope && !(base > 0.0)) || !(yarn_s >= 1.0))
     return -1;
   int64_t total = (int64_t)B * Hq * S;
   if (!rows) nrows = total;
@@ -226,7 +255,7 @@ int apex_oracle_prefill(const void* q, const void* k, const void* v, int dtype,
       }
       if (n == 0) continue;
       prefill_ctx c = {q, k, v, dtype, S, Hq, Hkv, d, causal, W, apply_rope, P, m0, base,
-                       b, kvh, krot, vd, all, slot, out, probs};
+                       yarn_s, b, kvh, krot, vd, all, slot, out, probs};
       parallel_for(S, nthreads, prefill_prepare_keys, &c);
       parallel_for(n, nthreads, prefill_rows, &c);
     }
@@ -240,7 +269,7 @@ typedef struct {
   const void *q, *kc, *vc, *kn, *vn;
   int dtype, Sk, Hq, Hkv, d, W, apply_rope;
   int64_t m;
-  double base;
+  double base, yarn_s;
   const int64_t* rows;  /* flat b*Hq + h */
   double* out;
 } decode_ctx;
@@ -255,12 +284,12 @@ static void decode_rows(void* p, int64_t lo, int64_t hi) {
   double* scores = (double*)malloc(sizeof(double) * n_max);
   const double** keys = (const double**)malloc(sizeof(double*) * n_max);
   const double** vals = (const double**)malloc(sizeof(double*) * n_max);
-  double scale = 1.0 / sqrt((double)d);
+  double scale = apex_oracle_yarn_attn_factor(c->yarn_s) / sqrt((double)d);
   for (int64_t r = lo; r < hi; r++) {
     int64_t bh = c->rows ? c->rows[r] : r;
     int64_t b = bh / c->Hq, h = bh % c->Hq, kvh = h / G;
     for (int t = 0; t < d; t++) q[t] = load_elem(c->q, c->dtype, bh * d + t);
-    if (c->apply_rope) apex_oracle_rope_row(q, q, d, c->m, c->base);
+    if (c->apply_rope) apex_oracle_rope_row(q, q, d, c->m, c->base, c->yarn_s);
     int64_t kv_row0 = (b * c->Hkv + kvh) * (int64_t)c->Sk;
     int64_t n = 0;
     for (int64_t j = 0; j <= c->m; j++) {
@@ -269,7 +298,7 @@ static void decode_rows(void* p, int64_t lo, int64_t hi) {
       double* vr = vd + n * d;
       if (j == c->m && c->kn) {
         for (int t = 0; t < d; t++) kr[t] = load_elem(c->kn, c->dtype, (b * c->Hkv + kvh) * d + t);
-        if (c->apply_rope) apex_oracle_rope_row(kr, kr, d, c->m, c->base);
+        if (c->apply_rope) apex_oracle_rope_row(kr, kr, d, c->m, c->base, c->yarn_s);
       } else {
         for (int t = 0; t < d; t++) kr[t] = load_elem(c->kc, c->dtype, (kv_row0 + j) * d + t);
       }
@@ -294,11 +323,11 @@ static void decode_rows(void* p, int64_t lo, int64_t hi) {
 int apex_oracle_decode(const void* q, const void* k_cache, const void* v_cache,
                        const void* k_new, const void* v_new, int dtype,
                        int B, int Sk, int Hq, int Hkv, int d, int W, int64_t m,
-                       double base, int apply_rope,
+                       double base, double yarn_s, int apply_rope,
                        int64_t nrows, const int64_t* rows, double* out, int nthreads) {
   if (!q || !k_cache || !v_cache || !out || B < 1 || Sk < 1 || Hq < 1 || Hkv < 1 ||
       Hq % Hkv || d < 2 || (d & 1) || W < 0 || m < 0 || m >= Sk ||
-      (dtype != 0 && dtype != 1) || (apply_rope && !(base > 0.0)))
+      (dtype != 0 && dtype != 1) || (apply_rope && !(base > 0.0)) || !(yarn_s >= 1.0))
     return -1;
   int64_t total = (int64_t)B * Hq;
   if (!rows) nrows = total;
@@ -307,7 +336,7 @@ int apex_oracle_decode(const void* q, const void* k_cache, const void* v_cache,
     if (f < 0 || f >= total) return -1;
   }
   decode_ctx c = {q, k_cache, v_cache, k_new, v_new, dtype, Sk, Hq, Hkv, d, W, apply_rope,
-                  m, base, rows, out};
+                  m, base, yarn_s, rows, out};
   parallel_for(nrows, nthreads, decode_rows, &c);
   return 0;
 }

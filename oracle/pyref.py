@@ -13,14 +13,27 @@ module, no arrays, so that every step can be read against the pages:
 import math
 
 
-def theta(d_h, base=10000.0):
-    return [base ** (-2.0 * i / d_h) for i in range(d_h // 2)]
+def yarn(th, s, beta_fast=32.0, beta_slow=1.0):
+    """YaRN frequency by wavelength regime (Part 1, §5.3-5.4), t clamped to [0, 1]."""
+    if s == 1:
+        return th
+    lam = 2 * math.pi / th
+    if lam < beta_fast:
+        return th
+    if lam > beta_slow * s:
+        return th / s
+    t = min(1.0, max(0.0, (lam / beta_slow - 1) / (s - 1)))
+    return th / (t * s + (1 - t))
 
 
-def rope(x, pos, base=10000.0):
+def theta(d_h, base=10000.0, s=1.0):
+    return [yarn(base ** (-2.0 * i / d_h), s) for i in range(d_h // 2)]
+
+
+def rope(x, pos, base=10000.0, s=1.0):
     d_h = len(x)
     y = list(x)
-    for i, th in enumerate(theta(d_h, base)):
+    for i, th in enumerate(theta(d_h, base, s)):
         c, s = math.cos(pos * th), math.sin(pos * th)
         a, b = x[2 * i], x[2 * i + 1]
         y[2 * i] = a * c - b * s
@@ -36,10 +49,10 @@ def visible(i, j, causal, W, P=0):
     return j <= i and (W == 0 or i - j < W)
 
 
-def sdpa_row(q, keys, vals):
-    """softmax(q.k_j / sqrt(d)) weighted sum of v_j, plus the weights."""
+def sdpa_row(q, keys, vals, factor=1.0):
+    """softmax(factor * q.k_j / sqrt(d)) weighted sum of v_j, plus the weights."""
     d = len(q)
-    scores = [sum(a * b for a, b in zip(q, k)) / math.sqrt(d) for k in keys]
+    scores = [factor * sum(a * b for a, b in zip(q, k)) / math.sqrt(d) for k in keys]
     mx = max(scores)
     w = [math.exp(s - mx) for s in scores]
     tot = sum(w)
@@ -53,7 +66,7 @@ def sdpa(Q, K, V):
     return [sdpa_row(q, K, V)[0] for q in Q]
 
 
-def prefill(q, k, v, causal=True, W=0, m0=0, base=10000.0, apply_rope=True, P=0):
+def prefill(q, k, v, causal=True, W=0, m0=0, base=10000.0, apply_rope=True, P=0, s=1.0):
     """q[B][Hq][S][d], k and v [B][Hkv][S][d] -> o[B][Hq][S][d]."""
     B, Hq, S = len(q), len(q[0]), len(q[0][0])
     Hkv = len(k[0])
@@ -63,13 +76,14 @@ def prefill(q, k, v, causal=True, W=0, m0=0, base=10000.0, apply_rope=True, P=0)
         heads = []
         for h in range(Hq):
             kvh = h // G
-            keys = [rope(k[b][kvh][j], m0 + j, base) if apply_rope else k[b][kvh][j]
+            keys = [rope(k[b][kvh][j], m0 + j, base, s) if apply_rope else k[b][kvh][j]
                     for j in range(S)]
             rows = []
             for i in range(S):
-                qi = rope(q[b][h][i], m0 + i, base) if apply_rope else q[b][h][i]
+                qi = rope(q[b][h][i], m0 + i, base, s) if apply_rope else q[b][h][i]
                 js = [j for j in range(S) if visible(i, j, causal, W, P)]
-                o, _ = sdpa_row(qi, [keys[j] for j in js], [v[b][kvh][j] for j in js])
+                o, _ = sdpa_row(qi, [keys[j] for j in js], [v[b][kvh][j] for j in js],
+                                0.1 * math.log(s) + 1.0)
                 rows.append(o)
             heads.append(rows)
         out.append(heads)

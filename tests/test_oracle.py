@@ -563,3 +563,88 @@ def test_rmsnorm_rejects():
         oracle.rmsnorm(_rand((2, 8)), _rand((7,)))
     with pytest.raises(ValueError):
         oracle.rmsnorm(_rand((2, 8)), _rand((8,)), eps=-1.0)
+
+
+# --------------------------------------------------------------------------
+# YaRN (Part 1, §5)
+# --------------------------------------------------------------------------
+def test_yarn_worked_example(golden_dir):
+    g = _golden(golden_dir, "rope_yarn_worked_example.json")
+    s = g["s"]
+    by_i = {p["i"]: p for p in g["pairs"]}
+    for p in g["pairs"]:
+        assert abs(2 * math.pi / p["theta"] - p["wavelength_printed"]) < 0.5
+    assert oracle.yarn_theta(by_i[0]["theta"], s) == by_i[0]["theta_yarn_printed"]  # high: kept
+    assert abs(oracle.yarn_theta(by_i[15]["theta"], s) - by_i[15]["theta_yarn_printed"]) < 1e-18
+    # mid band with t = (628 - 1) / 31 ~ 20.2 clamped to 1: theta / s
+    lam = 2 * math.pi / by_i[8]["theta"]
+    assert abs((lam - 1) / (s - 1) - by_i[8]["t_unclamped_printed"]) < 0.05
+    assert oracle.yarn_theta(by_i[8]["theta"], s) == pytest.approx(by_i[8]["theta"] / s, rel=1e-15)
+    assert abs(oracle.yarn_attn_factor(s) - g["attn_factor_printed"]) < 5e-4
+    assert oracle.yarn_attn_factor(s) == pytest.approx(0.1 * math.log(32) + 1, rel=1e-15)
+
+
+@pytest.mark.parametrize("s", [1.0, 4.0, 8.0, 32.0, 64.0, 1000.0])
+def test_yarn_regimes(s):
+    # the regime table: wavelength below 32 keeps theta, above s divides it
+    # by s, and between the two the divisor lies in [1, s]; s = 1 changes nothing
+    for th in np.geomspace(1e-7, 4.0, 400):
+        lam = 2 * math.pi / th
+        got = oracle.yarn_theta(th, s)
+        if s == 1.0 or lam < 32:
+            assert got == th
+        elif lam > s:
+            assert got == pytest.approx(th / s, rel=1e-15)
+        else:
+            assert th / s * (1 - 1e-15) <= got <= th * (1 + 1e-15)
+    assert oracle.yarn_attn_factor(1.0) == 1.0
+
+
+def test_yarn_mid_band_interpolation_formula():
+    # s = 64: wavelengths 32 .. 64 are interpolated with t = (lambda - 1) / 63
+    s = 64.0
+    for lam in (32.0, 40.0, 63.9):
+        th = 2 * math.pi / lam
+        t = (lam - 1) / (s - 1)
+        assert oracle.yarn_theta(th, s) == pytest.approx(th / (t * s + 1 - t), rel=1e-14)
+
+
+@pytest.mark.parametrize("s", [4.0, 64.0])
+def test_yarn_prefill_matches_torch_sdpa(s):
+    # RoPE with the YaRN frequencies as a complex rotation, then torch's SDPA
+    # with the scores multiplied by the temperature
+    S, Hq, Hkv, d = 21, 4, 2, 64
+    q, k, v = _rand((1, Hq, S, d)), _rand((1, Hkv, S, d)), _rand((1, Hkv, S, d))
+    got = oracle.prefill(q, k, v, causal=1, W=0, m0=5000, yarn_s=s)
+    qt, kt, vt = (torch.from_numpy(np.asarray(x, np.float64)) for x in (q, k, v))
+    th = torch.from_numpy(oracle.theta(d, 10000.0, s))
+    pos = torch.arange(S, dtype=torch.float64) + 5000
+    rot = torch.polar(torch.ones(S, d // 2, dtype=torch.float64), pos[:, None] * th)
+
+    def r(x):
+        z = torch.view_as_complex(x.reshape(*x.shape[:-1], d // 2, 2).contiguous()) * rot
+        return torch.view_as_real(z).reshape(x.shape)
+    qt, kt = r(qt), r(kt).repeat_interleave(Hq // Hkv, dim=1)
+    vt = vt.repeat_interleave(Hq // Hkv, dim=1)
+    mask = torch.from_numpy(_dense_mask(S, 1, 0))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, attn_mask=mask, scale=(0.1 * math.log(s) + 1) / math.sqrt(d)).numpy()
+    assert np.max(np.abs(got - ref)) <= 1e-10
+
+
+def test_yarn_c_oracle_matches_python_twin():
+    S, d = 9, 8
+    q, k, v = _rand((1, 2, S, d)), _rand((1, 1, S, d)), _rand((1, 1, S, d))
+    for s in (2.0, 40.0):
+        got = oracle.prefill(q, k, v, causal=1, m0=100, base=10.0, yarn_s=s)
+        ref = np.array(pyref.prefill(q.astype(float).tolist(), k.astype(float).tolist(),
+                                     v.astype(float).tolist(), True, 0, 100, 10.0, True, 0, s))
+        assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_yarn_rejects_scale_below_one():
+    q, k, v = _rand((1, 1, 4, 4)), _rand((1, 1, 4, 4)), _rand((1, 1, 4, 4))
+    with pytest.raises(ValueError):
+        oracle.prefill(q, k, v, yarn_s=0.5)
+    with pytest.raises(ValueError):
+        oracle.theta(8, 10000.0, 0.0)
