@@ -16,7 +16,8 @@ import torch
 # The workloads: name -> sizes. Symbols follow the pages' notation table
 # (Part 1, §1): B batch, S sequence, H_q / H_kv query / KV heads, d_h head
 # size, W window (0 = none), prefix P of the bidirectional prefix (absent = 0),
-# m0 position of row 0, base the RoPE base.
+# yarn_s the YaRN scale factor (absent = 1), m0 position of row 0, base the
+# RoPE base.
 WORKLOADS = {
     "tiny_prefill_f32": dict(kind="prefill", B=1, S=128, Hq=4, Hkv=2, d=64, causal=1, W=0,
                              m0=0, base=10000.0, dtype="f32", seed=1),
@@ -33,6 +34,10 @@ WORKLOADS = {
     "prefix_local_prefill_s16384_w4096_p1024": dict(kind="prefill", B=2, S=16384, Hq=32, Hkv=8,
                                                     d=128, causal=1, W=4096, prefix=1024, m0=0,
                                                     base=10000.0, dtype="bf16", seed=7),
+    # YaRN (Part 1, §5): an 8K-trained model run at 32K positions, s = 4
+    "yarn_local_prefill_s32768_w4096_s4": dict(kind="prefill", B=1, S=32768, Hq=32, Hkv=8, d=128,
+                                               causal=1, W=4096, yarn_s=4.0, m0=0, base=10000.0,
+                                               dtype="bf16", seed=10),
     # RMSNorm over d_model features (Part 1, §3); the pages' widths run 512 .. 7168
     "rmsnorm_b4_s2048_d7168": dict(kind="rmsnorm", B=4, S=2048, d=7168, eps=1e-6, dtype="bf16",
                                    seed=8),

@@ -33,7 +33,8 @@ HEADLINE = "gqa_prefill_s2048"
 DECODE = "gqa_decode_sk32768"
 RMSNORMS = ("rmsnorm_b4_s2048_d7168", "rmsnorm_b64_s2048_d512")
 OTHERS = ("window_prefill_s16384_w4096", "local_prefill_s65536_w512",
-          "prefix_prefill_s2048_p512", "prefix_local_prefill_s16384_w4096_p1024")
+          "prefix_prefill_s2048_p512", "prefix_local_prefill_s16384_w4096_p1024",
+          "yarn_local_prefill_s32768_w4096_s4")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_gqa_s2048_traffic.json")
 PREFILL_SOURCES = ("transformer_attention_amd/csrc/prefill_kernel.hpp",
                    "transformer_attention_amd/csrc/device_common.hpp")
@@ -110,12 +111,14 @@ def time_prefill(taa, torch, name, steps, warmup):
     w = apex_inputs.WORKLOADS[name]
     q, k, v = apex_inputs.workload_inputs(name, device="cuda")
     kr, o = torch.empty_like(k), torch.empty_like(q)
-    kw = dict(causal=w["causal"], W=w["W"], m0=w["m0"], base=w["base"], prefix=w.get("prefix", 0))
+    ys = w.get("yarn_s", 1.0)
+    kw = dict(causal=w["causal"], W=w["W"], m0=w["m0"], base=w["base"], prefix=w.get("prefix", 0),
+              yarn_s=ys)
 
     def step(ev=None):
         if ev:
             ev[0].record()
-        taa.apex_rope_qk(None, k, k_out=kr, m0=w["m0"], base=w["base"])
+        taa.apex_rope_qk(None, k, k_out=kr, m0=w["m0"], base=w["base"], yarn_s=ys)
         if ev:
             ev[1].record()
         taa.apex_attn_prefill(q, kr, v, o, None, apply_rope=2, **kw)

@@ -59,15 +59,21 @@ enum { APEX_F32 = 0, APEX_BF16 = 1 };
  *   and an output may equal its own input (in-place rotation) but must not
  *   overlap any other buffer.
  *   base: the RoPE base b (> 0), 10000 on the pages.
+ *   yarn_s: YaRN scale factor s >= 1 (Part 1, §5.3-5.4); 1 = plain RoPE.
+ *     Each frequency theta_i is replaced by its YaRN value with the pages'
+ *     defaults beta_fast = 32, beta_slow = 1: kept when its wavelength
+ *     2 pi / theta_i is below 32, divided by s when the wavelength exceeds s,
+ *     otherwise divided by t s + 1 - t, t = (wavelength - 1) / (s - 1)
+ *     clamped to [0, 1].
  * Angles are formed in fp64 and reduced to one turn before the fp32 sine and
  * cosine, so large positions keep full fp32 accuracy.
  * Errors: APEX_EINVAL for B or S < 1, H_q < 1 when q is given, H_kv < 1 when
- * k is given, a half-given pair, no pair, m0 < 0, base <= 0, an unknown
- * dtype; APEX_EUNSUPPORTED for d_h not 64 or 128.
+ * k is given, a half-given pair, no pair, m0 < 0, base <= 0, yarn_s < 1 or
+ * not finite, an unknown dtype; APEX_EUNSUPPORTED for d_h not 64 or 128.
  */
 int apex_rope_qk(const void* q, const void* k, void* q_out, void* k_out, int B, int S,
-                 int H_q, int H_kv, int d_h, int64_t m0, double base, int dtype,
-                 void* stream);
+                 int H_q, int H_kv, int d_h, int64_t m0, double base, double yarn_s,
+                 int dtype, void* stream);
 
 /*
  * apex_attn_prefill -- o = softmax(RoPE(q) RoPE(k)^T / sqrt(d_h)) v with GQA
@@ -83,6 +89,9 @@ int apex_rope_qk(const void* q, const void* k, void* q_out, void* k_out, int B, 
  *     bidirectional prefix: each sees exactly the keys j < P. Rows i >= P keep
  *     the causal mask and the window. 0 = no prefix.
  *   m0: position of row 0 (>= 0). The mask depends on row indices only.
+ *   base, yarn_s: the RoPE base and YaRN scale factor as for apex_rope_qk.
+ *     With yarn_s > 1 the scores are also multiplied by the YaRN attention
+ *     temperature 0.1 ln(yarn_s) + 1 (Part 1, §5.5), whatever apply_rope.
  *   apply_rope:
  *     1 = q and k are raw: k is rotated once into k_rope_out (one elementwise
  *         launch), then the attention launch rotates q while its tiles load
@@ -96,13 +105,13 @@ int apex_rope_qk(const void* q, const void* k, void* q_out, void* k_out, int B, 
  *     not overlap q, v or o.
  * Errors: APEX_EINVAL for H_q % H_kv != 0, sizes < 1, W < 0, W > 0 with
  * causal = 0, prefix < 0, prefix > 0 with causal = 0, m0 < 0, apply_rope not
- * 0/1/2, base <= 0 with apply_rope, a NULL required pointer, an unknown
- * dtype; APEX_EUNSUPPORTED for d_h not 64 or 128.
+ * 0/1/2, base <= 0 with apply_rope, yarn_s < 1 or not finite, a NULL
+ * required pointer, an unknown dtype; APEX_EUNSUPPORTED for d_h not 64 or 128.
  */
 int apex_attn_prefill(const void* q, const void* k, const void* v, void* o,
                       void* k_rope_out, int B, int S, int H_q, int H_kv, int d_h,
                       int causal, int W, int prefix, int64_t m0, double base,
-                      int apply_rope, int dtype, void* stream);
+                      double yarn_s, int apply_rope, int dtype, void* stream);
 
 /*
  * apex_rmsnorm -- y = x / sqrt(mean(x^2) + eps) * gamma over each row of d
@@ -137,17 +146,20 @@ size_t apex_attn_decode_workspace_bytes(int B, int H_q, int H_kv, int Sk, int d_
  *     NULL. When given, the rotated k_new (raw when apply_rope = 0) and v_new
  *     are written into slot m of the caches and used for slot m in this call.
  *   o: [B, H_q, 1, d_h] output.
+ *   base, yarn_s: as for apex_attn_prefill (YaRN frequencies for q and k_new,
+ *     the temperature on the scores when yarn_s > 1).
  *   workspace: device scratch of workspace_bytes >= the value returned by
  *     apex_attn_decode_workspace_bytes for the same sizes.
  * Errors: APEX_EINVAL for H_q % H_kv != 0, sizes < 1, W < 0, m < 0 or
- * m >= Sk, exactly one of k_new / v_new given, base <= 0 with apply_rope, a
- * NULL required pointer, an unknown dtype; APEX_EUNSUPPORTED for d_h not 64
- * or 128 or dtype fp32; APEX_EWORKSPACE when workspace is NULL or too small.
+ * m >= Sk, exactly one of k_new / v_new given, base <= 0 with apply_rope,
+ * yarn_s < 1 or not finite, a NULL required pointer, an unknown dtype;
+ * APEX_EUNSUPPORTED for d_h not 64 or 128 or dtype fp32; APEX_EWORKSPACE when
+ * workspace is NULL or too small.
  */
 int apex_attn_decode(const void* q, void* k_cache, void* v_cache,
                      const void* k_new, const void* v_new, void* o,
                      int B, int Sk, int H_q, int H_kv, int d_h, int W, int64_t m,
-                     double base, int apply_rope, void* workspace,
+                     double base, double yarn_s, int apply_rope, void* workspace,
                      size_t workspace_bytes, int dtype, void* stream);
 
 /* apex_strerror -- static text for a status code; never NULL. */

@@ -46,8 +46,9 @@ def test_strerror_covers_every_status(L):
     assert L.apex_strerror(-3).decode().startswith("decode workspace")
 
 
-def _rope(L, q=P, k=P, qo=P, ko=P, B=1, S=8, Hq=2, Hkv=1, d=64, m0=0, base=1e4, dtype=1):
-    return L.apex_rope_qk(q, k, qo, ko, B, S, Hq, Hkv, d, m0, base, dtype, None)
+def _rope(L, q=P, k=P, qo=P, ko=P, B=1, S=8, Hq=2, Hkv=1, d=64, m0=0, base=1e4, yarn=1.0,
+          dtype=1):
+    return L.apex_rope_qk(q, k, qo, ko, B, S, Hq, Hkv, d, m0, base, yarn, dtype, None)
 
 
 def test_rope_rejects(L):
@@ -63,6 +64,9 @@ def test_rope_rejects(L):
     assert _rope(L, m0=-1) == EINVAL
     assert _rope(L, base=0.0) == EINVAL
     assert _rope(L, base=-5.0) == EINVAL
+    assert _rope(L, yarn=0.5) == EINVAL
+    assert _rope(L, yarn=float("nan")) == EINVAL
+    assert _rope(L, yarn=float("inf")) == EINVAL
     assert _rope(L, dtype=7) == EINVAL
     assert _rope(L, d=63) == EINVAL
     assert _rope(L, d=96) == EUNSUP
@@ -73,9 +77,9 @@ def test_rope_rejects(L):
 
 
 def _prefill(L, q=P, k=P, v=P, o=P, kr=P, B=1, S=8, Hq=4, Hkv=2, d=128, causal=1, W=0, prefix=0,
-             m0=0, base=1e4, rope=1, dtype=1):
-    return L.apex_attn_prefill(q, k, v, o, kr, B, S, Hq, Hkv, d, causal, W, prefix, m0, base, rope,
-                               dtype, None)
+             m0=0, base=1e4, yarn=1.0, rope=1, dtype=1):
+    return L.apex_attn_prefill(q, k, v, o, kr, B, S, Hq, Hkv, d, causal, W, prefix, m0, base, yarn,
+                               rope, dtype, None)
 
 
 def test_prefill_rejects(L):
@@ -92,6 +96,8 @@ def test_prefill_rejects(L):
     assert _prefill(L, causal=2) == EINVAL
     assert _prefill(L, m0=-3) == EINVAL
     assert _prefill(L, base=0.0) == EINVAL
+    assert _prefill(L, yarn=0.99) == EINVAL
+    assert _prefill(L, yarn=0.5, rope=0) == EINVAL  # the temperature needs s >= 1 too
     assert _prefill(L, rope=3) == EINVAL
     assert _prefill(L, rope=-1) == EINVAL
     assert _prefill(L, dtype=2) == EINVAL
@@ -120,11 +126,11 @@ def test_decode_workspace_bytes(L):
 
 
 def _decode(L, q=P, kc=P, vc=P, kn=P, vn=P, o=P, B=2, Sk=64, Hq=16, Hkv=1, d=128, W=0, m=63,
-            base=1e4, rope=1, ws=P, wsb=None, dtype=1):
+            base=1e4, yarn=1.0, rope=1, ws=P, wsb=None, dtype=1):
     if wsb is None:
         wsb = L.apex_attn_decode_workspace_bytes(B, Hq, Hkv, Sk, d) if Hkv > 0 else 0
-    return L.apex_attn_decode(q, kc, vc, kn, vn, o, B, Sk, Hq, Hkv, d, W, m, base, rope, ws, wsb,
-                              dtype, None)
+    return L.apex_attn_decode(q, kc, vc, kn, vn, o, B, Sk, Hq, Hkv, d, W, m, base, yarn, rope, ws,
+                              wsb, dtype, None)
 
 
 def test_decode_rejects(L):
@@ -139,6 +145,7 @@ def test_decode_rejects(L):
     assert _decode(L, m=-1) == EINVAL
     assert _decode(L, m=64) == EINVAL       # m >= Sk
     assert _decode(L, base=-1.0) == EINVAL
+    assert _decode(L, yarn=0.0) == EINVAL
     assert _decode(L, rope=3) == EINVAL
     assert _decode(L, dtype=5) == EINVAL
     assert _decode(L, d=9) == EINVAL

@@ -86,6 +86,28 @@ def test_rope_matches_oracle(taa, dtype, d, m0):
             assert np.all(np.abs(g - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("s,m0", [(4.0, 30000), (40.0, 0), (64.0, 10 ** 6)])
+def test_rope_yarn_matches_oracle(taa, dtype, d, s, m0):
+    # s = 40 and 64 put some frequencies in YaRN's interpolated band
+    _say("rope yarn", dtype, d, s, m0)
+    q, k, _ = apex_inputs.prefill_inputs(1, 37, 2, 1, d, dtype, seed=13, device="cuda")
+    q0 = q.cpu()
+    taa.apex_rope_qk(q, None, m0=m0, yarn_s=s)
+    torch.cuda.synchronize()
+    x = q0.double().numpy()
+    ref = np.empty_like(x)
+    for h in range(x.shape[1]):
+        for r in range(x.shape[2]):
+            ref[0, h, r] = oracle.rope_row(x[0, h, r], m0 + r, yarn_s=s)
+    g = q.cpu().double().numpy()
+    if dtype == "f32":
+        assert np.max(np.abs(g - ref)) <= 1e-5
+    else:
+        assert np.all(np.abs(g - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6)
+
+
 # -------------------------------------------------------------- prefill ----
 PREFILL_CASES = [
     # B, S, Hq, Hkv, d, causal, W, m0, dtype, apply_rope
@@ -149,6 +171,29 @@ def test_prefill_prefix(taa, case):
     _check(o, ref, dtype, "prefill prefix %s" % (case,))
 
 
+YARN_CASES = [
+    # B, S, Hq, Hkv, d, W, m0, yarn_s, apply_rope, dtype
+    (1, 300, 8, 2, 128, 0, 5000, 4.0, 1, "bf16"),
+    (2, 129, 4, 1, 64, 50, 100000, 64.0, 1, "bf16"),
+    (1, 200, 8, 8, 128, 0, 0, 8.0, 0, "bf16"),   # temperature only: q, k given rotated
+    (1, 77, 4, 2, 64, 0, 30000, 40.0, 1, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", YARN_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_yarn(taa, case):
+    B, S, Hq, Hkv, d, W, m0, ys, rope, dtype = case
+    _say("prefill yarn", case)
+    q, k, v = apex_inputs.prefill_inputs(B, S, Hq, Hkv, d, dtype, seed=S + 3, device="cuda")
+    o = torch.empty_like(q)
+    kr = torch.empty_like(k)
+    taa.apex_attn_prefill(q, k, v, o, kr, causal=1, W=W, m0=m0, apply_rope=rope, yarn_s=ys)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), causal=1, W=W, m0=m0, apply_rope=rope,
+                         yarn_s=ys)
+    _check(o, ref, dtype, "prefill yarn %s" % (case,))
+
+
 def test_k_rope_out_holds_rotated_keys_and_may_alias_k(taa):
     B, S, Hq, Hkv, d = 1, 200, 8, 2, 128
     q, k, v = apex_inputs.prefill_inputs(B, S, Hq, Hkv, d, "bf16", seed=5, device="cuda")
@@ -186,18 +231,18 @@ def _run_prefill_workload(taa, name, n_random):
     _say("workload", name, w)
     q, k, v = apex_inputs.workload_inputs(name, device="cuda")
     o, kr = torch.empty_like(q), torch.empty_like(k)
-    P = w.get("prefix", 0)
+    P, ys = w.get("prefix", 0), w.get("yarn_s", 1.0)
     taa.apex_attn_prefill(q, k, v, o, kr, causal=w["causal"], W=w["W"], m0=w["m0"],
-                          base=w["base"], apply_rope=1, prefix=P)
+                          base=w["base"], apply_rope=1, prefix=P, yarn_s=ys)
     torch.cuda.synchronize()
     B, Hq, S, d = q.shape
     if n_random is None:
         ref = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), causal=w["causal"], W=w["W"],
-                             m0=w["m0"], base=w["base"], prefix=P)
+                             m0=w["m0"], base=w["base"], prefix=P, yarn_s=ys)
         return _check(o, ref, w["dtype"], name)
     rows = _rows(B, Hq, S, n_random, seed=w["seed"])
     ref = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), causal=w["causal"], W=w["W"], m0=w["m0"],
-                         base=w["base"], rows=rows, prefix=P)
+                         base=w["base"], rows=rows, prefix=P, yarn_s=ys)
     got = o.reshape(-1, d)[torch.from_numpy(rows).to(o.device)]
     return _check(got, ref, w["dtype"], "%s (%d sampled rows)" % (name, rows.size))
 
@@ -216,6 +261,10 @@ def test_workload_window_prefill_s16384_w4096(taa):
 
 def test_workload_local_prefill_s65536_w512(taa):
     _run_prefill_workload(taa, "local_prefill_s65536_w512", 3000)
+
+
+def test_workload_yarn_local_prefill_s32768_w4096_s4(taa):
+    _run_prefill_workload(taa, "yarn_local_prefill_s32768_w4096_s4", 2000)
 
 
 def test_workload_prefix_prefill_s2048_p512(taa):
@@ -272,6 +321,21 @@ def test_decode_small(taa, case):
                          for b in range(B)])
         got = kc1[:, :, m].double().numpy()
         assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -8 + 1e-6)
+
+
+@pytest.mark.parametrize("ys", [4.0, 64.0])
+def test_decode_yarn(taa, ys):
+    B, Sk, Hq, Hkv, d, m = 2, 3000, 16, 2, 128, 2999
+    _say("decode yarn", ys)
+    q, kc, vc, kn, vn = _decode_inputs(B, Sk, Hq, Hkv, d, seed=17)
+    kc0, vc0 = kc.cpu(), vc.cpu()
+    o = torch.empty_like(q)
+    ws = torch.empty(taa.apex_attn_decode_workspace_bytes(B, Hq, Hkv, Sk, d), dtype=torch.uint8,
+                     device="cuda")
+    taa.apex_attn_decode(q, kc, vc, kn, vn, o, m=m, workspace=ws, yarn_s=ys)
+    torch.cuda.synchronize()
+    ref = oracle.decode(q.cpu(), kc0, vc0, kn.cpu(), vn.cpu(), m=m, yarn_s=ys)
+    _check(o, ref, "bf16", "decode yarn %s" % ys)
 
 
 def test_decode_repeat_is_idempotent(taa):

@@ -35,17 +35,18 @@ def lib():
         L = ctypes.CDLL(_LIB)
         i32, i64, dbl, vp, sz = (ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p,
                                  ctypes.c_size_t)
-        L.apex_rope_qk.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, dbl, i32, vp]
+        L.apex_rope_qk.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, dbl, dbl, i32,
+                                   vp]
         L.apex_rope_qk.restype = i32
         L.apex_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
-                                        i64, dbl, i32, i32, vp]
+                                        i64, dbl, dbl, i32, i32, vp]
         L.apex_attn_prefill.restype = i32
         L.apex_rmsnorm.argtypes = [vp, vp, vp, i64, i32, dbl, i32, vp]
         L.apex_rmsnorm.restype = i32
         L.apex_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.apex_attn_decode_workspace_bytes.restype = sz
         L.apex_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
-                                       dbl, i32, vp, sz, i32, vp]
+                                       dbl, dbl, i32, vp, sz, i32, vp]
         L.apex_attn_decode.restype = i32
         L.apex_strerror.argtypes = [i32]
         L.apex_strerror.restype = ctypes.c_char_p
@@ -86,9 +87,9 @@ def _check(fn, status):
         raise ApexError(fn, status)
 
 
-def apex_rope_qk(q, k, q_out=None, k_out=None, m0=0, base=10000.0, stream=None):
+def apex_rope_qk(q, k, q_out=None, k_out=None, m0=0, base=10000.0, stream=None, yarn_s=1.0):
     """RoPE(q) -> q_out and RoPE(k) -> k_out; an output left None means in place.
-    q [B,H_q,S,d_h] or None, k [B,H_kv,S,d_h] or None."""
+    q [B,H_q,S,d_h] or None, k [B,H_kv,S,d_h] or None. yarn_s: YaRN scale factor."""
     if q is not None and q_out is None:
         q_out = q
     if k is not None and k_out is None:
@@ -98,21 +99,23 @@ def apex_rope_qk(q, k, q_out=None, k_out=None, m0=0, base=10000.0, stream=None):
     Hq = q.shape[1] if q is not None else 0
     Hkv = k.shape[1] if k is not None else 0
     _check("apex_rope_qk", lib().apex_rope_qk(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), B, S,
-                                              Hq, Hkv, d, int(m0), float(base), _dtype_code(t),
-                                              _stream(t, stream)))
+                                              Hq, Hkv, d, int(m0), float(base), float(yarn_s),
+                                              _dtype_code(t), _stream(t, stream)))
 
 
 def apex_attn_prefill(q, k, v, o, k_rope_out=None, causal=1, W=0, m0=0, base=10000.0,
-                      apply_rope=1, stream=None, prefix=0):
+                      apply_rope=1, stream=None, prefix=0, yarn_s=1.0):
     """o = softmax(RoPE(q) RoPE(k)^T / sqrt(d_h)) v. apply_rope: 1 = rotate q and k
     (RoPE(k) lands in k_rope_out), 2 = rotate q only (k holds rotated keys), 0 = none.
-    prefix: rows i < prefix see exactly the keys j < prefix (bidirectional prefix)."""
+    prefix: rows i < prefix see exactly the keys j < prefix (bidirectional prefix).
+    yarn_s: YaRN scale factor (frequencies, and the score temperature when > 1)."""
     B, Hq, S, d = q.shape
     Hkv = k.shape[1]
     _check("apex_attn_prefill",
            lib().apex_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(k_rope_out), B, S, Hq,
                                    Hkv, d, int(causal), int(W), int(prefix), int(m0), float(base),
-                                   int(apply_rope), _dtype_code(q), _stream(q, stream)))
+                                   float(yarn_s), int(apply_rope), _dtype_code(q),
+                                   _stream(q, stream)))
 
 
 def apex_rmsnorm(x, gamma, y=None, eps=1e-6, stream=None):
@@ -133,7 +136,7 @@ def apex_attn_decode_workspace_bytes(B, H_q, H_kv, Sk, d_h):
 
 
 def apex_attn_decode(q, k_cache, v_cache, k_new, v_new, o, m, W=0, base=10000.0, apply_rope=1,
-                     workspace=None, stream=None):
+                     workspace=None, stream=None, yarn_s=1.0):
     """One query per (b, h) at position m against [B,H_kv,Sk,d_h] caches."""
     B, Hq, _, d = q.shape
     Hkv, Sk = k_cache.shape[1], k_cache.shape[2]
@@ -141,5 +144,6 @@ def apex_attn_decode(q, k_cache, v_cache, k_new, v_new, o, m, W=0, base=10000.0,
     _check("apex_attn_decode",
            lib().apex_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
                                   _ptr(o), B, Sk, Hq, Hkv, d, int(W), int(m), float(base),
-                                  int(apply_rope), _ptr(workspace), nbytes, _dtype_code(q),
+                                  float(yarn_s), int(apply_rope), _ptr(workspace), nbytes,
+                                  _dtype_code(q),
                                   _stream(q, stream)))

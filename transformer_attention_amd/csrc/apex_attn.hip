@@ -19,6 +19,12 @@ constexpr double kLog2e = 1.4426950408889634074;
 
 bool head_size_ok(int d_h) { return d_h == 64 || d_h == 128; }
 
+// A YaRN scale factor: >= 1 and finite (1 = plain RoPE).
+bool yarn_ok(double s) { return s >= 1.0 && s <= 1e30; }
+
+// The YaRN attention temperature 0.1 ln(s) + 1 (Part 1, §5.5); 1 for s = 1.
+double yarn_attn_factor(double s) { return 0.1 * log(s) + 1.0; }
+
 int check_dims(int d_h, int dtype) {
   if (d_h < 2 || (d_h & 1)) return APEX_EINVAL;
   if (dtype != APEX_F32 && dtype != APEX_BF16) return APEX_EINVAL;
@@ -31,8 +37,8 @@ int launch_status() {
 }
 
 int launch_rope(const void* src, void* dst, long long n_bh, int S, int d_h, int64_t m0,
-                double base, int dtype, hipStream_t st) {
-  apex::RopeParams p{src, dst, n_bh, S, d_h, (long long)m0, base};
+                double base, double yarn_s, int dtype, hipStream_t st) {
+  apex::RopeParams p{src, dst, n_bh, S, d_h, (long long)m0, base, yarn_s};
   const long long work = n_bh * ((S + apex::kRopeRows - 1) / apex::kRopeRows) * (d_h / 8);
   long long blocks = (work + apex::kRopeThreads - 1) / apex::kRopeThreads;
   if (blocks > 65535LL * 16) blocks = 65535LL * 16;
@@ -95,29 +101,34 @@ const char* apex_strerror(int status) {
 }
 
 int apex_rope_qk(const void* q, const void* k, void* q_out, void* k_out, int B, int S, int H_q,
-                 int H_kv, int d_h, int64_t m0, double base, int dtype, void* stream) {
+                 int H_kv, int d_h, int64_t m0, double base, double yarn_s, int dtype,
+                 void* stream) {
   if ((q == nullptr) != (q_out == nullptr) || (k == nullptr) != (k_out == nullptr) || (!q && !k))
     return APEX_EINVAL;
-  if (B < 1 || S < 1 || (q && H_q < 1) || (k && H_kv < 1) || m0 < 0 || !(base > 0.0))
+  if (B < 1 || S < 1 || (q && H_q < 1) || (k && H_kv < 1) || m0 < 0 || !(base > 0.0) ||
+      !yarn_ok(yarn_s))
     return APEX_EINVAL;
   const int dc = check_dims(d_h, dtype);
   if (dc != APEX_OK) return dc;
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
   int rc = APEX_OK;
-  if (q) rc = launch_rope(q, q_out, (long long)B * H_q, S, d_h, m0, base, dtype, st);
-  if (rc == APEX_OK && k) rc = launch_rope(k, k_out, (long long)B * H_kv, S, d_h, m0, base, dtype, st);
+  if (q) rc = launch_rope(q, q_out, (long long)B * H_q, S, d_h, m0, base, yarn_s, dtype, st);
+  if (rc == APEX_OK && k)
+    rc = launch_rope(k, k_out, (long long)B * H_kv, S, d_h, m0, base, yarn_s, dtype, st);
   return rc;
 }
 
 int apex_attn_prefill(const void* q, const void* k, const void* v, void* o, void* k_rope_out,
                       int B, int S, int H_q, int H_kv, int d_h, int causal, int W, int prefix,
-                      int64_t m0, double base, int apply_rope, int dtype, void* stream) {
+                      int64_t m0, double base, double yarn_s, int apply_rope, int dtype,
+                      void* stream) {
   if (!q || !k || !v || !o || (apply_rope == 1 && !k_rope_out)) return APEX_EINVAL;
   if (B < 1 || S < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0) return APEX_EINVAL;
   if (W < 0 || (W > 0 && !causal) || (causal != 0 && causal != 1)) return APEX_EINVAL;
   if (prefix < 0 || (prefix > 0 && !causal)) return APEX_EINVAL;
-  if (m0 < 0 || apply_rope < 0 || apply_rope > 2 || (apply_rope && !(base > 0.0)))
+  if (m0 < 0 || apply_rope < 0 || apply_rope > 2 || (apply_rope && !(base > 0.0)) ||
+      !yarn_ok(yarn_s))
     return APEX_EINVAL;
   const int dc = check_dims(d_h, dtype);
   if (dc != APEX_OK) return dc;
@@ -126,7 +137,8 @@ int apex_attn_prefill(const void* q, const void* k, const void* v, void* o, void
 
   const void* kr = k;
   if (apply_rope == 1) {
-    const int rc = launch_rope(k, k_rope_out, (long long)B * H_kv, S, d_h, m0, base, dtype, st);
+    const int rc =
+        launch_rope(k, k_rope_out, (long long)B * H_kv, S, d_h, m0, base, yarn_s, dtype, st);
     if (rc != APEX_OK) return rc;
     kr = k_rope_out;
   }
@@ -139,13 +151,13 @@ int apex_attn_prefill(const void* q, const void* k, const void* v, void* o, void
     p.o = (uint16_t*)o;
     p.S = S; p.Hq = H_q; p.Hkv = H_kv; p.G = G;
     p.causal = causal; p.W = W; p.P = prefix < S ? prefix : S;
-    p.m0 = m0; p.base = base; p.apply_rope = apply_rope != 0;
+    p.m0 = m0; p.base = base; p.yarn_s = yarn_s; p.apply_rope = apply_rope != 0;
     p.g_pack = head_pack(G);
     p.bm = apex::kPfRows / p.g_pack;
     p.n_pos_tiles = (S + p.bm - 1) / p.bm;
     p.n_head_packs = G / p.g_pack;
     p.n_groups = B * H_kv * p.n_head_packs;
-    p.sc = (float)(kLog2e / sqrt((double)d_h));
+    p.sc = (float)(kLog2e * yarn_attn_factor(yarn_s) / sqrt((double)d_h));
     const long long blocks = (long long)p.n_pos_tiles * p.n_groups;
     if (blocks > 0x7fffffffLL) return APEX_EUNSUPPORTED;
     if (d_h == 128)
@@ -162,8 +174,8 @@ int apex_attn_prefill(const void* q, const void* k, const void* v, void* o, void
     p.o = (float*)o;
     p.S = S; p.Hq = H_q; p.Hkv = H_kv; p.G = G;
     p.causal = causal; p.W = W; p.P = prefix < S ? prefix : S;
-    p.m0 = m0; p.base = base; p.apply_rope = apply_rope != 0;
-    p.scale = (float)(1.0 / sqrt((double)d_h));
+    p.m0 = m0; p.base = base; p.yarn_s = yarn_s; p.apply_rope = apply_rope != 0;
+    p.scale = (float)(yarn_attn_factor(yarn_s) / sqrt((double)d_h));
     if (B > 65535 || H_q > 65535) return APEX_EUNSUPPORTED;
     const dim3 grid((S + apex::kF32Rows - 1) / apex::kF32Rows, H_q, B);
     if (d_h == 128)
@@ -198,12 +210,13 @@ size_t apex_attn_decode_workspace_bytes(int B, int H_q, int H_kv, int Sk, int d_
 
 int apex_attn_decode(const void* q, void* k_cache, void* v_cache, const void* k_new,
                      const void* v_new, void* o, int B, int Sk, int H_q, int H_kv, int d_h, int W,
-                     int64_t m, double base, int apply_rope, void* workspace,
+                     int64_t m, double base, double yarn_s, int apply_rope, void* workspace,
                      size_t workspace_bytes, int dtype, void* stream) {
   if (!q || !k_cache || !v_cache || !o || ((k_new == nullptr) != (v_new == nullptr)))
     return APEX_EINVAL;
   if (B < 1 || Sk < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || W < 0) return APEX_EINVAL;
-  if (m < 0 || m >= Sk || (apply_rope != 0 && apply_rope != 1) || (apply_rope && !(base > 0.0)))
+  if (m < 0 || m >= Sk || (apply_rope != 0 && apply_rope != 1) || (apply_rope && !(base > 0.0)) ||
+      !yarn_ok(yarn_s))
     return APEX_EINVAL;
   const int dc = check_dims(d_h, dtype);
   if (dc != APEX_OK) return dc;
@@ -232,11 +245,11 @@ int apex_attn_decode(const void* q, void* k_cache, void* v_cache, const void* k_
   p.ws_o = (float*)workspace;
   p.ws_ml = p.ws_o + (size_t)B * H_q * n_parts * d_h;
   p.Sk = Sk; p.Hq = H_q; p.Hkv = H_kv; p.G = G;
-  p.m = m; p.base = base; p.apply_rope = apply_rope;
+  p.m = m; p.base = base; p.yarn_s = yarn_s; p.apply_rope = apply_rope;
   p.n_hb = n_hb; p.n_parts = n_parts;
   p.key_lo = (int)key_lo;
   p.keys_per_part = (int)kpp;
-  p.sc = (float)(kLog2e / sqrt((double)d_h));
+  p.sc = (float)(kLog2e * yarn_attn_factor(yarn_s) / sqrt((double)d_h));
   const dim3 grid(n_split, H_kv * n_hb, B);
   if (d_h == 128)
     hipLaunchKernelGGL(apex::decode_split_kernel<128>, grid, dim3(apex::kDecThreads), 0, st, p);

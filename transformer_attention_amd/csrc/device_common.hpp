@@ -90,9 +90,21 @@ __device__ __forceinline__ void buffer_to_lds16(buffer_rsrc, uint32_t, APEX_LDS 
 #endif
 
 // ---- RoPE angles -------------------------------------------------------------
-// turns_i = theta_i / (2 pi) with theta_i = b^(-2i/d_h) (fp64).
-__device__ __forceinline__ double rope_turns(int i, int d_h, double base) {
-  return pow(base, -2.0 * (double)i / (double)d_h) * kInvTwoPi;
+// YaRN (Part 1, §5.3-5.4) at scale factor s >= 1 with beta_fast = 32 and
+// beta_slow = 1: by the wavelength 2 pi / theta, a frequency below 32 stays,
+// one above s is divided by s, and one in between is divided by t s + 1 - t
+// with t = (wavelength - 1) / (s - 1) held to [0, 1]. s = 1: unchanged.
+__device__ __forceinline__ double yarn_theta(double theta, double s) {
+  if (s == 1.0) return theta;
+  const double wavelength = 1.0 / (theta * kInvTwoPi);
+  if (wavelength < 32.0) return theta;
+  if (wavelength > s) return theta / s;
+  const double t = fmin(fmax((wavelength - 1.0) / (s - 1.0), 0.0), 1.0);
+  return theta / (t * s + (1.0 - t));
+}
+// turns_i = theta_i / (2 pi) with theta_i = b^(-2i/d_h) after YaRN (fp64).
+__device__ __forceinline__ double rope_turns(int i, int d_h, double base, double yarn_s) {
+  return yarn_theta(pow(base, -2.0 * (double)i / (double)d_h), yarn_s) * kInvTwoPi;
 }
 // The angle pos * theta_i is formed in fp64 as turns and reduced to [-1/2, 1/2]
 // before any fp32 step, so large positions lose no accuracy.

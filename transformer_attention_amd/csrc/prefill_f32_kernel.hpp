@@ -28,6 +28,7 @@ struct PrefillF32Params {
   int P;              // prefix rows (bidirectional within [0, P)); <= S
   long long m0;
   double base;
+  double yarn_s;      // YaRN scale factor (1 = plain RoPE)
   int apply_rope;
   float scale;  // 1 / sqrt(d_h)
 };
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(kF32Threads) void prefill_f32_kernel(PrefillF32Para
   const int kvh = h / p.G;
 
   if (p.apply_rope) {
-    if (tid < D / 2) turns_lds[tid] = rope_turns(tid, D, p.base);
+    if (tid < D / 2) turns_lds[tid] = rope_turns(tid, D, p.base, p.yarn_s);
     __syncthreads();
   }
 

@@ -62,6 +62,7 @@ struct PrefillParams {
   int P;              // prefix rows (bidirectional within [0, P)); <= S
   long long m0;
   double base;
+  double yarn_s;      // YaRN scale factor (1 = plain RoPE)
   int apply_rope;     // rotate q while it loads
   int g_pack;         // query heads per workgroup (divides G, <= kPfWaves)
   int bm;             // positions per workgroup = kPfRows / g_pack
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
   issue_tile(vg, vbuf[0], t_lo);
   if (t_lo < t_hi) issue_tile(kg, kbuf[1], t_lo + 1);
 
-  if (p.apply_rope && tid < D / 2) turns_lds[tid] = rope_turns(tid, D, p.base);
+  if (p.apply_rope && tid < D / 2) turns_lds[tid] = rope_turns(tid, D, p.base, p.yarn_s);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's tile loads have landed
   __syncthreads();                                    // ... and every other wave's
 

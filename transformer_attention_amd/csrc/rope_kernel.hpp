@@ -26,6 +26,7 @@ struct RopeParams {
   int d_h;
   long long m0;
   double base;
+  double yarn_s;      // YaRN scale factor (1 = plain RoPE)
 };
 
 template <typename T>
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeParams p) {
   __shared__ double turns_lds[128];  // theta_i / (2 pi), i < d_h / 2 <= 128
   __shared__ float step_c[128], step_s[128];  // cos, sin of theta_i (one position)
   if ((int)threadIdx.x < p.d_h / 2) {
-    const double turns = rope_turns(threadIdx.x, p.d_h, p.base);
+    const double turns = rope_turns(threadIdx.x, p.d_h, p.base, p.yarn_s);
     turns_lds[threadIdx.x] = turns;
     rope_cs_accurate(1, turns, step_c[threadIdx.x], step_s[threadIdx.x]);
   }
