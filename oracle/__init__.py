@@ -51,6 +51,8 @@ def lib():
         L.apex_oracle_prefill.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                           i64, i64, dbl, dbl, i32, i64, vp, vp, vp, i32]
         L.apex_oracle_rmsnorm.argtypes = [vp, vp, i32, i64, i32, dbl, vp, i32]
+        L.apex_oracle_prefill_mla.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                              i32, i64, i64, dbl, dbl, i32, i64, vp, vp, vp, i32]
         L.apex_oracle_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                          i64, dbl, dbl, i32, i64, vp, vp, i32]
         _lib = L
@@ -203,3 +205,38 @@ def rmsnorm(x, gamma, eps=1e-6, nthreads=None):
                                  nthreads or default_threads()) != 0:
         raise ValueError("apex_oracle_rmsnorm rejected its arguments")
     return out
+
+
+def prefill_mla(q, k, v, d_r, causal=True, W=0, m0=0, base=10000.0, apply_rope=True,
+                rows=None, probs=False, nthreads=None, prefix=0, yarn_s=1.0):
+    """MLA attention with decoupled RoPE: q [B,Hq,S,d_h+d_r], k [B,Hkv,S,d_h+d_r]
+    ([content | rope] rows, RoPE on the last d_r), v [B,Hkv,S,d_h]. Returns fp64
+    [B,Hq,S,d_h] (or [len(rows), d_h]), and the softmax weights if probs."""
+    qa, dt = _as_input(q)
+    ka, dk = _as_input(k)
+    va, dv_ = _as_input(v)
+    if not (dt == dk == dv_):
+        raise TypeError("q, k, v must share a dtype")
+    B, Hq, S, dqk = qa.shape
+    Hkv, d_h = ka.shape[1], va.shape[3]
+    if ka.shape != (B, Hkv, S, dqk) or va.shape != (B, Hkv, S, d_h) or dqk != d_h + d_r:
+        raise ValueError("shape mismatch")
+    if rows is None:
+        nrows, rarr = B * Hq * S, None
+    else:
+        rarr = np.ascontiguousarray(rows, np.int64)
+        nrows = rarr.size
+    out = np.empty((nrows, d_h), np.float64)
+    pr = np.empty((nrows, S), np.float64) if probs else None
+    rc = lib().apex_oracle_prefill_mla(_ptr(qa), _ptr(ka), _ptr(va), dt, B, S, Hq, Hkv, d_h,
+                                       int(d_r), int(causal), int(W), int(prefix), int(m0),
+                                       float(base), float(yarn_s), int(apply_rope), nrows,
+                                       _ptr(rarr), _ptr(out), _ptr(pr),
+                                       nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("apex_oracle_prefill_mla rejected its arguments")
+    if rows is None:
+        out = out.reshape(B, Hq, S, d_h)
+        if probs:
+            pr = pr.reshape(B, Hq, S, S)
+    return (out, pr) if probs else out

@@ -22,6 +22,10 @@
  *   - GQA: G = H_q/H_kv, query head h reads KV head floor(h/G)  (Part 2, §8.2).
  *   - Window mask: key j is visible to query i iff 0 <= i-j < W and j <= i
  *     (Part 2, §10.2). W = 0 means no window. Non-causal: every key visible.
+ *   - MLA attention with decoupled RoPE (Part 2, §9.3): q and k rows are
+ *     [content (d_h) | rope (d_r)], RoPE rotates only the rope part with the
+ *     frequencies of a d_r-dimensional head, v rows have d_h values, and the
+ *     scores are scaled by 1 / sqrt(d_h + d_r), the width of the dot product.
  *   - RMSNorm (Part 1, §3.2): y = x / sqrt(mean(x^2) + eps) * gamma over each
  *     row of d features.
  *   - Prefix-bidirectional regime (Part 2, §11.1, picture in §11.3): with a
@@ -114,7 +118,8 @@ int apex_oracle_visible(int64_t i, int64_t j, int causal, int64_t W, int64_t P) 
  * keys[j], vals[j] point at rows of length d. probs (optional) receives the
  * n weights.  (Part 2, §6.2) */
 static void attend(const double* q, const double* const* keys, const double* const* vals,
-                   int64_t n, int d, double scale, double* scores, double* out, double* probs) {
+                   int64_t n, int d, int dv, double scale, double* scores, double* out,
+                   double* probs) {
   double mx = -INFINITY;
   for (int64_t j = 0; j < n; j++) {
     double dot = 0.0;
@@ -127,11 +132,11 @@ static void attend(const double* q, const double* const* keys, const double* con
     scores[j] = exp(scores[j] - mx);
     sum += scores[j];
   }
-  for (int t = 0; t < d; t++) out[t] = 0.0;
+  for (int t = 0; t < dv; t++) out[t] = 0.0;
   for (int64_t j = 0; j < n; j++) {
     double w = scores[j] / sum;
     if (probs) probs[j] = w;
-    for (int t = 0; t < d; t++) out[t] += w * vals[j][t];
+    for (int t = 0; t < dv; t++) out[t] += w * vals[j][t];
   }
 }
 
@@ -161,7 +166,7 @@ static void parallel_for(int64_t n, int nthreads, range_fn fn, void* ctx) {
 /* ---------------------------- prefill ---------------------------- */
 typedef struct {
   const void *q, *k, *v;
-  int dtype, S, Hq, Hkv, d, causal, W, apply_rope;
+  int dtype, S, Hq, Hkv, d, dv, r_off, d_rope, causal, W, apply_rope;
   int64_t P, m0;
   double base, yarn_s;
   int b, kvh;
@@ -177,12 +182,11 @@ static void prefill_prepare_keys(void* p, int64_t lo, int64_t hi) {
   int64_t kv_off = ((int64_t)c->b * c->Hkv + c->kvh) * c->S;
   for (int64_t j = lo; j < hi; j++) {
     double* kr = c->krot + j * c->d;
-    double* vr = c->vd + j * c->d;
-    for (int t = 0; t < c->d; t++) {
-      kr[t] = load_elem(c->k, c->dtype, (kv_off + j) * c->d + t);
-      vr[t] = load_elem(c->v, c->dtype, (kv_off + j) * c->d + t);
-    }
-    if (c->apply_rope) apex_oracle_rope_row(kr, kr, c->d, c->m0 + j, c->base, c->yarn_s);
+    double* vr = c->vd + j * c->dv;
+    for (int t = 0; t < c->d; t++) kr[t] = load_elem(c->k, c->dtype, (kv_off + j) * c->d + t);
+    for (int t = 0; t < c->dv; t++) vr[t] = load_elem(c->v, c->dtype, (kv_off + j) * c->dv + t);
+    if (c->apply_rope)
+      apex_oracle_rope_row(kr + c->r_off, kr + c->r_off, c->d_rope, c->m0 + j, c->base, c->yarn_s);
   }
 }
 
@@ -199,17 +203,18 @@ static void prefill_rows(void* p, int64_t lo, int64_t hi) {
     int64_t flat = c->rows[r];                 /* (b*Hq + h)*S + i */
     int64_t i = flat % c->S;
     for (int t = 0; t < c->d; t++) q[t] = load_elem(c->q, c->dtype, flat * c->d + t);
-    if (c->apply_rope) apex_oracle_rope_row(q, q, c->d, c->m0 + i, c->base, c->yarn_s);
+    if (c->apply_rope)
+      apex_oracle_rope_row(q + c->r_off, q + c->r_off, c->d_rope, c->m0 + i, c->base, c->yarn_s);
     int64_t n = 0;
     for (int64_t j = 0; j < c->S; j++) {
       if (!apex_oracle_visible(i, j, c->causal, c->W, c->P)) continue;
       keys[n] = c->krot + j * c->d;
-      vals[n] = c->vd + j * c->d;
+      vals[n] = c->vd + j * c->dv;
       idx[n] = j;
       n++;
     }
-    double* o = c->out + c->row_slot[r] * c->d;
-    attend(q, keys, vals, n, c->d, scale, scores, o, c->probs ? pr : NULL);
+    double* o = c->out + c->row_slot[r] * c->dv;
+    attend(q, keys, vals, n, c->d, c->dv, scale, scores, o, c->probs ? pr : NULL);
     if (c->probs) {
       double* prow = c->probs + c->row_slot[r] * c->S;
       for (int64_t j = 0; j < c->S; j++) prow[j] = 0.0;
@@ -219,19 +224,22 @@ static void prefill_rows(void* p, int64_t lo, int64_t hi) {
   free(q); free(scores); free(keys); free(vals); free(idx); free(pr);
 }
 
-/* Attention output rows of a prefill. q [B,Hq,S,d], k and v [B,Hkv,S,d]
- * (row-major, fp32 or bf16 bits). rows: flat indices (b*Hq+h)*S+i of the rows
- * to compute, or NULL for all rows in order. out: [nrows, d] doubles.
- * P: prefix length (0: none; needs causal). probs: optional [nrows, S]
- * softmax weights (0 for masked keys).
+/* Attention output rows of a prefill, general form: q [B,Hq,S,dqk], k
+ * [B,Hkv,S,dqk], v [B,Hkv,S,dv] (row-major, fp32 or bf16 bits); RoPE rotates
+ * dims [r_off, r_off + d_rope) of q and k with the frequencies of a
+ * d_rope-dimensional head; scores scaled by attn_factor(yarn_s) / sqrt(dqk).
+ * rows: flat indices (b*Hq+h)*S+i of the rows to compute, or NULL for all
+ * rows in order. out: [nrows, dv] doubles. P: prefix length (0: none; needs
+ * causal). probs: optional [nrows, S] softmax weights (0 for masked keys).
  * Returns 0, or -1 on invalid arguments. */
-int apex_oracle_prefill(const void* q, const void* k, const void* v, int dtype,
-                        int B, int S, int Hq, int Hkv, int d, int causal, int W,
-                        int64_t P, int64_t m0, double base, double yarn_s, int apply_rope,
-                        int64_t nrows, const int64_t* rows, double* out, double* probs,
-                        int nthreads) {
+static int prefill_general(const void* q, const void* k, const void* v, int dtype,
+                           int B, int S, int Hq, int Hkv, int dqk, int dv, int r_off, int d_rope,
+                           int causal, int W, int64_t P, int64_t m0, double base, double yarn_s,
+                           int apply_rope, int64_t nrows, const int64_t* rows, double* out,
+                           double* probs, int nthreads) {
   if (!q || !k || !v || !out || B < 1 || S < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv ||
-      d < 2 || (d & 1) || W < 0 || (W > 0 && !causal) || P < 0 || (P > 0 && !causal) ||
+      dqk < 1 || dv < 1 || d_rope < 2 || (d_rope & 1) || r_off < 0 || r_off + d_rope > dqk ||
+      W < 0 || (W > 0 && !causal) || P < 0 || (P > 0 && !causal) ||
       (dtype != 0 && dtype != 1) || (apply_rope && !(base > 0.0)) || !(yarn_s >= 1.0))
     return -1;
   int64_t total = (int64_t)B * Hq * S;
@@ -239,8 +247,8 @@ int apex_oracle_prefill(const void* q, const void* k, const void* v, int dtype,
   int G = Hq / Hkv;
   int64_t* all = (int64_t*)malloc(sizeof(int64_t) * (nrows > 0 ? nrows : 1));
   int64_t* slot = (int64_t*)malloc(sizeof(int64_t) * (nrows > 0 ? nrows : 1));
-  double* krot = (double*)malloc(sizeof(double) * (size_t)S * d);
-  double* vd = (double*)malloc(sizeof(double) * (size_t)S * d);
+  double* krot = (double*)malloc(sizeof(double) * (size_t)S * dqk);
+  double* vd = (double*)malloc(sizeof(double) * (size_t)S * dv);
   for (int64_t r = 0; r < nrows; r++) {
     int64_t f = rows ? rows[r] : r;
     if (f < 0 || f >= total) { free(all); free(slot); free(krot); free(vd); return -1; }
@@ -254,14 +262,38 @@ int apex_oracle_prefill(const void* q, const void* k, const void* v, int dtype,
         if (bh / Hq == b && (bh % Hq) / G == kvh) { all[n] = f; slot[n] = r; n++; }
       }
       if (n == 0) continue;
-      prefill_ctx c = {q, k, v, dtype, S, Hq, Hkv, d, causal, W, apply_rope, P, m0, base,
-                       yarn_s, b, kvh, krot, vd, all, slot, out, probs};
+      prefill_ctx c = {q, k, v, dtype, S, Hq, Hkv, dqk, dv, r_off, d_rope, causal, W, apply_rope,
+                       P, m0, base, yarn_s, b, kvh, krot, vd, all, slot, out, probs};
       parallel_for(S, nthreads, prefill_prepare_keys, &c);
       parallel_for(n, nthreads, prefill_rows, &c);
     }
   }
   free(all); free(slot); free(krot); free(vd);
   return 0;
+}
+
+/* Prefill with q, k, v, out rows of d values and RoPE over the whole row. */
+int apex_oracle_prefill(const void* q, const void* k, const void* v, int dtype,
+                        int B, int S, int Hq, int Hkv, int d, int causal, int W,
+                        int64_t P, int64_t m0, double base, double yarn_s, int apply_rope,
+                        int64_t nrows, const int64_t* rows, double* out, double* probs,
+                        int nthreads) {
+  if (d < 2 || (d & 1)) return -1;
+  return prefill_general(q, k, v, dtype, B, S, Hq, Hkv, d, d, 0, d, causal, W, P, m0, base,
+                         yarn_s, apply_rope, nrows, rows, out, probs, nthreads);
+}
+
+/* MLA prefill with decoupled RoPE (Part 2, §9.3): q and k rows of
+ * d_h + d_r values, [content | rope], RoPE on the last d_r; v and out rows of
+ * d_h values; scale 1 / sqrt(d_h + d_r). */
+int apex_oracle_prefill_mla(const void* q, const void* k, const void* v, int dtype,
+                            int B, int S, int Hq, int Hkv, int d_h, int d_r, int causal, int W,
+                            int64_t P, int64_t m0, double base, double yarn_s, int apply_rope,
+                            int64_t nrows, const int64_t* rows, double* out, double* probs,
+                            int nthreads) {
+  if (d_h < 1) return -1;
+  return prefill_general(q, k, v, dtype, B, S, Hq, Hkv, d_h + d_r, d_h, d_h, d_r, causal, W, P,
+                         m0, base, yarn_s, apply_rope, nrows, rows, out, probs, nthreads);
 }
 
 /* ----------------------------- decode ----------------------------- */
@@ -311,7 +343,7 @@ static void decode_rows(void* p, int64_t lo, int64_t hi) {
       vals[n] = vr;
       n++;
     }
-    attend(q, keys, vals, n, d, scale, scores, c->out + r * d, NULL);
+    attend(q, keys, vals, n, d, d, scale, scores, c->out + r * d, NULL);
   }
   free(q); free(kd); free(vd); free(scores); free(keys); free(vals);
 }

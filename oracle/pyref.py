@@ -125,3 +125,32 @@ def rmsnorm(x, gamma, eps=1e-6):
         rms = math.sqrt(sum(v * v for v in row) / len(row) + eps)
         out.append([v / rms * g for v, g in zip(row, gamma)])
     return out
+
+
+def prefill_mla(q, k, v, d_r, causal=True, W=0, m0=0, base=10000.0, P=0, s=1.0):
+    """MLA with decoupled RoPE: q, k rows [content | rope(d_r)], v rows of d_h."""
+    B, Hq, S = len(q), len(q[0]), len(q[0][0])
+    Hkv = len(k[0])
+    G = Hq // Hkv
+    dqk = len(q[0][0][0])
+    dh = dqk - d_r
+
+    def rot(x, pos):
+        return list(x[:dh]) + rope(x[dh:], pos, base, s)
+    out = []
+    for b in range(B):
+        heads = []
+        for h in range(Hq):
+            kvh = h // G
+            keys = [rot(k[b][kvh][j], m0 + j) for j in range(S)]
+            rows = []
+            for i in range(S):
+                qi = rot(q[b][h][i], m0 + i)
+                js = [j for j in range(S) if visible(i, j, causal, W, P)]
+                # sdpa_row scales by 1/sqrt(len(q)) = 1/sqrt(d_h + d_r)
+                o, _ = sdpa_row(qi, [keys[j] for j in js], [v[b][kvh][j] for j in js],
+                                0.1 * math.log(s) + 1.0)
+                rows.append(o)
+            heads.append(rows)
+        out.append(heads)
+    return out

@@ -648,3 +648,78 @@ def test_yarn_rejects_scale_below_one():
         oracle.prefill(q, k, v, yarn_s=0.5)
     with pytest.raises(ValueError):
         oracle.theta(8, 10000.0, 0.0)
+
+
+# --------------------------------------------------------------------------
+# MLA attention with decoupled RoPE (Part 2, §9.3)
+# --------------------------------------------------------------------------
+def _torch_mla_reference(q, k, v, d_r, m0, base, W=0):
+    """torch SDPA in float64 on [content | RoPE(rope part)] rows, RoPE of the
+    rope part as a complex rotation with d_r-dimensional frequencies, scale
+    1 / sqrt(d_h + d_r)."""
+    q, k, v = (torch.from_numpy(np.asarray(x, np.float64)) for x in (q, k, v))
+    B, Hq, S, dqk = q.shape
+    G = Hq // k.shape[1]
+    dh = dqk - d_r
+    pos = torch.arange(S, dtype=torch.float64) + m0
+    theta = base ** (-torch.arange(0, d_r, 2, dtype=torch.float64) / d_r)
+    rot = torch.polar(torch.ones(S, d_r // 2, dtype=torch.float64), pos[:, None] * theta)
+
+    def r(x):
+        xr = x[..., dh:]
+        z = torch.view_as_complex(xr.reshape(*xr.shape[:-1], d_r // 2, 2).contiguous()) * rot
+        return torch.cat([x[..., :dh], torch.view_as_real(z).reshape(xr.shape)], -1)
+    q, k = r(q), r(k).repeat_interleave(G, dim=1)
+    v = v.repeat_interleave(G, dim=1)
+    mask = torch.from_numpy(_dense_mask(S, 1, W))
+    return torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, attn_mask=mask, scale=1.0 / math.sqrt(dqk)).numpy()
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,d_h,d_r,W,m0", [
+    (1, 2, 1, 8, 4, 0, 0),
+    (19, 4, 2, 16, 8, 0, 100),
+    (33, 4, 1, 32, 16, 7, 5000),
+    (24, 2, 2, 128, 64, 0, 3),
+])
+def test_mla_matches_torch_sdpa(S, Hq, Hkv, d_h, d_r, W, m0):
+    q = _rand((1, Hq, S, d_h + d_r))
+    k = _rand((1, Hkv, S, d_h + d_r))
+    v = _rand((1, Hkv, S, d_h))
+    got = oracle.prefill_mla(q, k, v, d_r, causal=1, W=W, m0=m0)
+    ref = _torch_mla_reference(q, k, v, d_r, m0, 10000.0, W)
+    assert np.max(np.abs(got - ref)) <= 1e-10
+
+
+def test_mla_rope_touches_only_the_rope_part():
+    # rotating the whole row instead of the last d_r would change the result;
+    # with a zero rope part the positions drop out entirely
+    S, d_h, d_r = 17, 16, 8
+    q, k, v = _rand((1, 2, S, d_h + d_r)), _rand((1, 1, S, d_h + d_r)), _rand((1, 1, S, d_h))
+    q[..., d_h:] = 0
+    k[..., d_h:] = 0
+    a = oracle.prefill_mla(q, k, v, d_r, m0=0)
+    b = oracle.prefill_mla(q, k, v, d_r, m0=12345)
+    assert np.max(np.abs(a - b)) <= 1e-13
+    # and then the result is plain attention on the content part, scaled by
+    # 1 / sqrt(d_h + d_r): the same as content scaled by sqrt(d_h / (d_h + d_r))
+    qs = (q[..., :d_h].astype(np.float64) * math.sqrt(d_h / (d_h + d_r)))
+    ref = _torch_reference(qs, k[..., :d_h], v, 1, 0, 0, 10000.0, False)
+    assert np.max(np.abs(a - ref)) <= 1e-10
+
+
+def test_mla_scores_depend_on_relative_position_only():
+    S, d_h, d_r = 21, 16, 16
+    q, k, v = _rand((1, 2, S, d_h + d_r)), _rand((1, 1, S, d_h + d_r)), _rand((1, 1, S, d_h))
+    a = oracle.prefill_mla(q, k, v, d_r, m0=0)
+    b = oracle.prefill_mla(q, k, v, d_r, m0=777)
+    assert np.max(np.abs(a - b)) <= 1e-9
+
+
+def test_mla_c_oracle_matches_python_twin():
+    S, d_h, d_r = 8, 6, 4
+    q, k, v = _rand((1, 2, S, d_h + d_r)), _rand((1, 1, S, d_h + d_r)), _rand((1, 1, S, d_h))
+    got = oracle.prefill_mla(q, k, v, d_r, causal=1, W=3, m0=11, prefix=2, yarn_s=2.0)
+    ref = np.array(pyref.prefill_mla(q.astype(float).tolist(), k.astype(float).tolist(),
+                                     v.astype(float).tolist(), d_r, True, 3, 11, 10000.0, 2, 2.0))
+    assert np.max(np.abs(got - ref)) <= 1e-12
