@@ -15,9 +15,9 @@ import torch
 
 # The workloads: name -> sizes. Symbols follow the pages' notation table
 # (Part 1, §1): B batch, S sequence, H_q / H_kv query / KV heads, d_h head
-# size, W window (0 = none), prefix P of the bidirectional prefix (absent = 0),
-# yarn_s the YaRN scale factor (absent = 1), m0 position of row 0, base the
-# RoPE base.
+# size, d_r the RoPE part of an MLA head, W window (0 = none), prefix P of the
+# bidirectional prefix (absent = 0), yarn_s the YaRN scale factor (absent = 1),
+# m0 position of row 0, base the RoPE base.
 WORKLOADS = {
     "tiny_prefill_f32": dict(kind="prefill", B=1, S=128, Hq=4, Hkv=2, d=64, causal=1, W=0,
                              m0=0, base=10000.0, dtype="f32", seed=1),
@@ -38,6 +38,11 @@ WORKLOADS = {
     "yarn_local_prefill_s32768_w4096_s4": dict(kind="prefill", B=1, S=32768, Hq=32, Hkv=8, d=128,
                                                causal=1, W=4096, yarn_s=4.0, m0=0, base=10000.0,
                                                dtype="bf16", seed=10),
+    # MLA global layer (Part 2, §9.3, §11.2): [content d_h | rope d_r] queries and keys,
+    # full causal attention over the whole sequence
+    "mla_global_prefill_s16384": dict(kind="mla_prefill", B=1, S=16384, Hq=64, Hkv=8, d=128,
+                                      d_r=64, causal=1, W=0, m0=0, base=10000.0, dtype="bf16",
+                                      seed=11),
     # RMSNorm over d_model features (Part 1, §3); the pages' widths run 512 .. 7168
     "rmsnorm_b4_s2048_d7168": dict(kind="rmsnorm", B=4, S=2048, d=7168, eps=1e-6, dtype="bf16",
                                    seed=8),
@@ -74,6 +79,15 @@ def prefill_inputs(B, S, Hq, Hkv, d, dtype="bf16", seed=0, device="cpu"):
     return q, k, v
 
 
+def mla_prefill_inputs(B, S, Hq, Hkv, d, d_r, dtype="bf16", seed=0, device="cpu"):
+    """(q [B,Hq,S,d+d_r], k [B,Hkv,S,d+d_r], v [B,Hkv,S,d]): [content | rope] rows."""
+    dt = TORCH_DTYPE[dtype] if isinstance(dtype, str) else dtype
+    q = normal((B, Hq, S, d + d_r), seed * 16 + 0, dt, device)
+    k = normal((B, Hkv, S, d + d_r), seed * 16 + 1, dt, device)
+    v = normal((B, Hkv, S, d), seed * 16 + 2, dt, device)
+    return q, k, v
+
+
 def decode_inputs(B, Sk, Hq, Hkv, d, dtype="bf16", seed=0, device="cpu"):
     """(q [B,Hq,1,d], k_cache, v_cache [B,Hkv,Sk,d], k_new, v_new [B,Hkv,1,d]).
 
@@ -101,6 +115,9 @@ def workload_inputs(name, device="cpu"):
     w = WORKLOADS[name]
     if w["kind"] == "rmsnorm":
         return rmsnorm_inputs(w["B"], w["S"], w["d"], w["dtype"], w["seed"], device)
+    if w["kind"] == "mla_prefill":
+        return mla_prefill_inputs(w["B"], w["S"], w["Hq"], w["Hkv"], w["d"], w["d_r"], w["dtype"],
+                                  w["seed"], device)
     if w["kind"] == "prefill":
         return prefill_inputs(w["B"], w["S"], w["Hq"], w["Hkv"], w["d"], w["dtype"], w["seed"],
                               device)

@@ -34,7 +34,7 @@ DECODE = "gqa_decode_sk32768"
 RMSNORMS = ("rmsnorm_b4_s2048_d7168", "rmsnorm_b64_s2048_d512")
 OTHERS = ("window_prefill_s16384_w4096", "local_prefill_s65536_w512",
           "prefix_prefill_s2048_p512", "prefix_local_prefill_s16384_w4096_p1024",
-          "yarn_local_prefill_s32768_w4096_s4")
+          "yarn_local_prefill_s32768_w4096_s4", "mla_global_prefill_s16384")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_gqa_s2048_traffic.json")
 PREFILL_SOURCES = ("transformer_attention_amd/csrc/prefill_kernel.hpp",
                    "transformer_attention_amd/csrc/device_common.hpp")
@@ -62,14 +62,18 @@ def n_visible(S, causal, W, P=0):
 
 
 def prefill_flops(w):
-    return 4 * w["B"] * w["Hq"] * w["d"] * n_visible(w["S"], w["causal"], w["W"],
-                                                     w.get("prefix", 0))
+    """2 FLOPs per multiply-add of q.k (d_h + d_r wide; d_r = 0 outside MLA)
+    and of p.v (d_h wide), per visible pair and query head."""
+    width = 2 * w["d"] + w.get("d_r", 0)
+    return 2 * width * w["B"] * w["Hq"] * n_visible(w["S"], w["causal"], w["W"],
+                                                    w.get("prefix", 0))
 
 
 def prefill_bytes(w):
     """Algorithmic HBM bytes of the attention launch: q, k, v read once, o written once."""
     e = 2 if w["dtype"] == "bf16" else 4
-    return e * w["d"] * w["S"] * w["B"] * (2 * w["Hq"] + 2 * w["Hkv"])
+    dqk, dv = w["d"] + w.get("d_r", 0), w["d"]
+    return e * w["S"] * w["B"] * (w["Hq"] * (dqk + dv) + w["Hkv"] * (dqk + dv))
 
 
 def decode_bytes(w):
@@ -115,13 +119,21 @@ def time_prefill(taa, torch, name, steps, warmup):
     kw = dict(causal=w["causal"], W=w["W"], m0=w["m0"], base=w["base"], prefix=w.get("prefix", 0),
               yarn_s=ys)
 
+    if w["kind"] == "mla_prefill":
+        # the MLA call rotates the key rope parts and runs the attention in one call
+        o = torch.empty(q.shape[:3] + (w["d"],), dtype=q.dtype, device=q.device)
+
     def step(ev=None):
         if ev:
             ev[0].record()
-        taa.apex_rope_qk(None, k, k_out=kr, m0=w["m0"], base=w["base"], yarn_s=ys)
+        if w["kind"] != "mla_prefill":
+            taa.apex_rope_qk(None, k, k_out=kr, m0=w["m0"], base=w["base"], yarn_s=ys)
         if ev:
             ev[1].record()
-        taa.apex_attn_prefill(q, kr, v, o, None, apply_rope=2, **kw)
+        if w["kind"] == "mla_prefill":
+            taa.apex_attn_prefill_mla(q, k, v, o, kr, apply_rope=1, **kw)
+        else:
+            taa.apex_attn_prefill(q, kr, v, o, None, apply_rope=2, **kw)
         if ev:
             ev[2].record()
 
@@ -244,7 +256,7 @@ def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     WRITE_SIZE runs scaled by what the same counters read for the calibration
     copy (read 1 GiB, write 1 GiB), into profiles/ next to the source hash."""
     f = lambda d: os.path.join(d, "p_counter_collection.csv")
-    kname = "prefill_bf16_kernel<128>"
+    kname = "prefill_bf16_kernel<128, 128, 128>"
     fetch, nf = _pmc_per_dispatch(f(fetch_dir), kname)
     write, nw = _pmc_per_dispatch(f(write_dir), kname)
     cf, _ = _pmc_per_dispatch(f(copy_fetch_dir), "neg_kernel")
@@ -338,6 +350,9 @@ def main():
                             "attention_tflops": round(of / (oattn * 1e-3) / 1e12, 1),
                             "frac_of_bf16_peak": round(of / (oms * 1e-3) / 1e12
                                                        / PEAK_BF16_TFLOPS, 4)}
+            if ow["kind"] == "mla_prefill":
+                others[name]["note"] = ("one apex_attn_prefill_mla call: attention_ms includes "
+                                        "its key RoPE launch")
         extra["other_workloads"] = others
         torch.cuda.empty_cache()
         norms = {}
@@ -370,7 +385,7 @@ def main():
                    "H_kv": w["Hkv"], "d_h": w["d"], "causal": w["causal"], "W": w["W"],
                    "rope_base": w["base"], "mask_adjusted_flops": flops},
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "roofline": {"kernel": "prefill_bf16_kernel<128>", "bound": "mfma",
+        "roofline": {"kernel": "prefill_bf16_kernel<128, 128, 128>", "bound": "mfma",
                      "achieved": round(attn_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": load_traffic(), "launch_ms_mean": round(attn_ms, 4),

@@ -114,6 +114,35 @@ int apex_attn_prefill(const void* q, const void* k, const void* v, void* o,
                       double yarn_s, int apply_rope, int dtype, void* stream);
 
 /*
+ * apex_attn_prefill_mla -- the attention core of multi-head latent attention
+ * with decoupled RoPE (Part 2, §9.3; used by the global layers, §11.2). Each
+ * query and key row is the concatenation [content (d_h) | rope (d_r)]; only
+ * the last d_r dims carry position, rotated as in apex_rope_qk with the
+ * frequencies of a d_r-wide head (theta_i = b^(-2i/d_r)). Values and outputs
+ * are d_h wide:
+ *   o = softmax(q' k'^T / sqrt(d_h + d_r)) v,  x' = [x_content | RoPE(x_rope)]
+ * (the pages leave the scale open; the score is a dot product over all
+ * d_h + d_r dims, and its variance is what the 1/sqrt(width) of §6.2 undoes).
+ *   q: [B, H_q, S, d_h + d_r]   (read only)
+ *   k: [B, H_kv, S, d_h + d_r]  (read only; query head h reads KV head
+ *      floor(h / G) as in apex_attn_prefill, rope part included)
+ *   v: [B, H_kv, S, d_h]        (read only)
+ *   o: [B, H_q, S, d_h]         output; must not overlap any input.
+ *   k_rope_out: [B, H_kv, S, d_h + d_r] receives k' when apply_rope = 1 (the
+ *     content part copied, the rope part rotated). It may equal k (then only
+ *     the rope part is rewritten) but must not overlap q, v or o.
+ *   causal, W, prefix, m0, base, yarn_s, apply_rope, dtype, stream: as for
+ *   apex_attn_prefill (the YaRN frequencies follow d_r).
+ * Built for bf16 with d_h = 128, d_r = 64.
+ * Errors: as apex_attn_prefill, with d_h and d_r each even and >= 2
+ * (APEX_EINVAL otherwise); APEX_EUNSUPPORTED for any other (d_h, d_r) or fp32.
+ */
+int apex_attn_prefill_mla(const void* q, const void* k, const void* v, void* o,
+                          void* k_rope_out, int B, int S, int H_q, int H_kv, int d_h,
+                          int d_r, int causal, int W, int prefix, int64_t m0, double base,
+                          double yarn_s, int apply_rope, int dtype, void* stream);
+
+/*
  * apex_rmsnorm -- y = x / sqrt(mean(x^2) + eps) * gamma over each row of d
  * features (Part 1, §3.2; the norm in front of attention, §3.5).
  *   x: [rows, d] row-major (read only unless y == x).

@@ -30,8 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["apex_attn_decode", "apex_attn_decode_workspace_bytes",
-                                    "apex_attn_prefill", "apex_rmsnorm", "apex_rope_qk",
-                                    "apex_strerror"]
+                                    "apex_attn_prefill", "apex_attn_prefill_mla", "apex_rmsnorm",
+                                    "apex_rope_qk", "apex_strerror"]
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -112,6 +112,34 @@ def test_prefill_rope_modes_and_rope_buffer(L):
     assert _prefill(L, kr=None, rope=0, base=0.0, d=96) == EUNSUP  # base unused without RoPE
     assert _prefill(L, kr=None, rope=2, d=96) == EUNSUP            # q-only RoPE: no buffer
     assert _prefill(L, kr=None, rope=2, base=0.0) == EINVAL
+
+
+def _mla(L, q=P, k=P, v=P, o=P, kr=P, B=1, S=8, Hq=4, Hkv=2, d=128, dr=64, causal=1, W=0,
+         prefix=0, m0=0, base=1e4, yarn=1.0, rope=1, dtype=1):
+    return L.apex_attn_prefill_mla(q, k, v, o, kr, B, S, Hq, Hkv, d, dr, causal, W, prefix, m0,
+                                   base, yarn, rope, dtype, None)
+
+
+def test_prefill_mla_rejects(L):
+    for kw in (dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(kr=None)):
+        assert _mla(L, **kw) == EINVAL, kw
+    assert _mla(L, kr=None, rope=2, d=64) == EUNSUP   # no RoPE buffer needed
+    assert _mla(L, Hq=3, Hkv=2) == EINVAL
+    assert _mla(L, B=0) == EINVAL
+    assert _mla(L, S=0) == EINVAL
+    assert _mla(L, causal=0, W=4) == EINVAL
+    assert _mla(L, causal=0, prefix=2) == EINVAL
+    assert _mla(L, m0=-1) == EINVAL
+    assert _mla(L, base=-1.0) == EINVAL
+    assert _mla(L, yarn=0.0) == EINVAL
+    assert _mla(L, rope=3) == EINVAL
+    assert _mla(L, dtype=2) == EINVAL
+    assert _mla(L, d=127) == EINVAL
+    assert _mla(L, dr=0) == EINVAL
+    assert _mla(L, dr=63) == EINVAL
+    assert _mla(L, d=64) == EUNSUP      # built for d_h = 128, d_r = 64
+    assert _mla(L, dr=32) == EUNSUP
+    assert _mla(L, dtype=0) == EUNSUP   # and for bf16
 
 
 def test_decode_workspace_bytes(L):

@@ -225,6 +225,59 @@ def test_fused_rope_agrees_with_prerotated_inputs(taa):
     _check(o_pre, ref, "bf16", "pre-rotated")
 
 
+# ------------------------------------------------------------------ MLA ----
+MLA_CASES = [
+    # B, S, Hq, Hkv, causal, W, prefix, m0, yarn_s, apply_rope -- d_h 128, d_r 64
+    (1, 1, 2, 1, 1, 0, 0, 0, 1.0, 1),
+    (1, 3, 4, 4, 1, 0, 0, 9, 1.0, 1),
+    (1, 65, 8, 2, 1, 0, 0, 0, 1.0, 1),
+    (2, 300, 16, 4, 1, 0, 0, 1000, 1.0, 1),
+    (1, 513, 8, 8, 0, 0, 0, 0, 1.0, 1),        # no mask, ragged tail
+    (1, 700, 32, 8, 1, 128, 0, 0, 1.0, 1),     # a window, tile skipping
+    (1, 640, 64, 8, 1, 0, 200, 0, 1.0, 1),     # prefix-bidirectional
+    (1, 257, 8, 2, 1, 0, 0, 20000, 8.0, 1),    # YaRN frequencies over d_r, temperature
+    (1, 200, 8, 2, 1, 0, 0, 0, 1.0, 0),        # q, k given rotated
+]
+
+
+@pytest.mark.parametrize("case", MLA_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_mla(taa, case):
+    B, S, Hq, Hkv, causal, W, P, m0, ys, rope = case
+    _say("prefill mla", case)
+    q, k, v = apex_inputs.mla_prefill_inputs(B, S, Hq, Hkv, 128, 64, "bf16", seed=S + Hq + 1,
+                                             device="cuda")
+    o = torch.empty(B, Hq, S, 128, dtype=torch.bfloat16, device="cuda")
+    kr = torch.empty_like(k)
+    taa.apex_attn_prefill_mla(q, k, v, o, kr, causal=causal, W=W, prefix=P, m0=m0,
+                              apply_rope=rope, yarn_s=ys)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_mla(q.cpu(), k.cpu(), v.cpu(), 64, causal=causal, W=W, prefix=P, m0=m0,
+                             apply_rope=rope, yarn_s=ys)
+    _check(o, ref, "bf16", "prefill mla %s" % (case,))
+
+
+def test_mla_rope_buffer_rotates_only_the_rope_part(taa):
+    B, S, Hq, Hkv = 1, 130, 4, 2
+    q, k, v = apex_inputs.mla_prefill_inputs(B, S, Hq, Hkv, 128, 64, "bf16", seed=12,
+                                             device="cuda")
+    o1 = torch.empty(B, Hq, S, 128, dtype=torch.bfloat16, device="cuda")
+    kr = torch.empty_like(k)
+    taa.apex_attn_prefill_mla(q, k, v, o1, kr, m0=77)
+    torch.cuda.synchronize()
+    assert torch.equal(kr[..., :128], k[..., :128])  # content part copied bit for bit
+    kr_rope = kr[..., 128:].double().cpu().numpy()
+    k_rope = k[..., 128:].double().cpu().numpy()
+    for h in range(Hkv):
+        for s_ in range(S):
+            want = oracle.rope_row(k_rope[0, h, s_], 77 + s_)
+            assert np.all(np.abs(kr_rope[0, h, s_] - want) <= np.abs(want) * 2.0 ** -8 + 1e-6)
+    o2 = torch.empty_like(o1)
+    k2 = k.clone()
+    taa.apex_attn_prefill_mla(q, k2, v, o2, k2, m0=77)  # in place: only the rope part moves
+    torch.cuda.synchronize()
+    assert torch.equal(k2, kr) and torch.equal(o1, o2)
+
+
 # ------------------------------------------------------ full workloads ----
 def _run_prefill_workload(taa, name, n_random):
     w = apex_inputs.WORKLOADS[name]
@@ -273,6 +326,24 @@ def test_workload_prefix_prefill_s2048_p512(taa):
 
 def test_workload_prefix_local_prefill_s16384_w4096_p1024(taa):
     _run_prefill_workload(taa, "prefix_local_prefill_s16384_w4096_p1024", 1500)
+
+
+def test_workload_mla_global_prefill_s16384(taa):
+    name = "mla_global_prefill_s16384"
+    w = apex_inputs.WORKLOADS[name]
+    _say("workload", name, w)
+    q, k, v = apex_inputs.workload_inputs(name, device="cuda")
+    B, Hq, S, _ = q.shape
+    o = torch.empty(B, Hq, S, w["d"], dtype=q.dtype, device="cuda")
+    kr = torch.empty_like(k)
+    taa.apex_attn_prefill_mla(q, k, v, o, kr, causal=w["causal"], W=w["W"], m0=w["m0"],
+                              base=w["base"])
+    torch.cuda.synchronize()
+    rows = _rows(B, Hq, S, 1500, seed=w["seed"])
+    ref = oracle.prefill_mla(q.cpu(), k.cpu(), v.cpu(), w["d_r"], causal=w["causal"], W=w["W"],
+                             m0=w["m0"], base=w["base"], rows=rows)
+    got = o.reshape(-1, w["d"])[torch.from_numpy(rows).to(o.device)]
+    _check(got, ref, w["dtype"], "%s (%d sampled rows)" % (name, rows.size))
 
 
 # --------------------------------------------------------------- decode ----

@@ -1,4 +1,4 @@
-"""MI355X (gfx950) RoPE + GQA / causal / sliding-window attention, and RMSNorm.
+"""MI355X (gfx950) RoPE + GQA / causal / sliding-window / MLA attention, and RMSNorm.
 
 The compute runs in the HIP kernels of ``libapex_attn.so``; this package only
 marshals torch tensors (device memory and the current stream) into its C ABI
@@ -6,5 +6,6 @@ marshals torch tensors (device memory and the current stream) into its C ABI
 every call raises.
 """
 from ._binding import (APEX_BF16, APEX_F32, ApexError, apex_attn_decode,  # noqa: F401
-                       apex_attn_decode_workspace_bytes, apex_attn_prefill, apex_rmsnorm,
-                       apex_rope_qk, apex_strerror, lib, lib_path)
+                       apex_attn_decode_workspace_bytes, apex_attn_prefill,
+                       apex_attn_prefill_mla, apex_rmsnorm, apex_rope_qk, apex_strerror, lib,
+                       lib_path)

@@ -41,6 +41,9 @@ def lib():
         L.apex_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                         i64, dbl, dbl, i32, i32, vp]
         L.apex_attn_prefill.restype = i32
+        L.apex_attn_prefill_mla.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                            i32, i32, i64, dbl, dbl, i32, i32, vp]
+        L.apex_attn_prefill_mla.restype = i32
         L.apex_rmsnorm.argtypes = [vp, vp, vp, i64, i32, dbl, i32, vp]
         L.apex_rmsnorm.restype = i32
         L.apex_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -116,6 +119,19 @@ def apex_attn_prefill(q, k, v, o, k_rope_out=None, causal=1, W=0, m0=0, base=100
                                    Hkv, d, int(causal), int(W), int(prefix), int(m0), float(base),
                                    float(yarn_s), int(apply_rope), _dtype_code(q),
                                    _stream(q, stream)))
+
+
+def apex_attn_prefill_mla(q, k, v, o, k_rope_out=None, causal=1, W=0, m0=0, base=10000.0,
+                          apply_rope=1, stream=None, prefix=0, yarn_s=1.0):
+    """MLA attention with decoupled RoPE: q, k rows are [content (d_h) | rope (d_r)],
+    v and o rows d_h wide; d_r = q width - v width. Other arguments as apex_attn_prefill."""
+    B, Hq, S, dqk = q.shape
+    Hkv, d_h = k.shape[1], v.shape[3]
+    _check("apex_attn_prefill_mla",
+           lib().apex_attn_prefill_mla(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(k_rope_out), B, S,
+                                       Hq, Hkv, d_h, dqk - d_h, int(causal), int(W), int(prefix),
+                                       int(m0), float(base), float(yarn_s), int(apply_rope),
+                                       _dtype_code(q), _stream(q, stream)))
 
 
 def apex_rmsnorm(x, gamma, y=None, eps=1e-6, stream=None):

@@ -36,10 +36,12 @@ int launch_status() {
   return hipGetLastError() == hipSuccess ? APEX_OK : APEX_EHIP;
 }
 
-int launch_rope(const void* src, void* dst, long long n_bh, int S, int d_h, int64_t m0,
-                double base, double yarn_s, int dtype, hipStream_t st) {
-  apex::RopeParams p{src, dst, n_bh, S, d_h, (long long)m0, base, yarn_s};
-  const long long work = n_bh * ((S + apex::kRopeRows - 1) / apex::kRopeRows) * (d_h / 8);
+// RoPE over rows of row_len elements whose last d_h turn (row_len = d_h for
+// the standard layers).
+int launch_rope(const void* src, void* dst, long long n_bh, int S, int d_h, int row_len,
+                int64_t m0, double base, double yarn_s, int dtype, hipStream_t st) {
+  apex::RopeParams p{src, dst, n_bh, S, d_h, row_len, (long long)m0, base, yarn_s};
+  const long long work = n_bh * ((S + apex::kRopeRows - 1) / apex::kRopeRows) * (row_len / 8);
   long long blocks = (work + apex::kRopeThreads - 1) / apex::kRopeThreads;
   if (blocks > 65535LL * 16) blocks = 65535LL * 16;
   if (blocks < 1) blocks = 1;
@@ -113,9 +115,9 @@ int apex_rope_qk(const void* q, const void* k, void* q_out, void* k_out, int B, 
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
   int rc = APEX_OK;
-  if (q) rc = launch_rope(q, q_out, (long long)B * H_q, S, d_h, m0, base, yarn_s, dtype, st);
+  if (q) rc = launch_rope(q, q_out, (long long)B * H_q, S, d_h, d_h, m0, base, yarn_s, dtype, st);
   if (rc == APEX_OK && k)
-    rc = launch_rope(k, k_out, (long long)B * H_kv, S, d_h, m0, base, yarn_s, dtype, st);
+    rc = launch_rope(k, k_out, (long long)B * H_kv, S, d_h, d_h, m0, base, yarn_s, dtype, st);
   return rc;
 }
 
@@ -137,8 +139,8 @@ int apex_attn_prefill(const void* q, const void* k, const void* v, void* o, void
 
   const void* kr = k;
   if (apply_rope == 1) {
-    const int rc =
-        launch_rope(k, k_rope_out, (long long)B * H_kv, S, d_h, m0, base, yarn_s, dtype, st);
+    const int rc = launch_rope(k, k_rope_out, (long long)B * H_kv, S, d_h, d_h, m0, base, yarn_s,
+                               dtype, st);
     if (rc != APEX_OK) return rc;
     kr = k_rope_out;
   }
@@ -161,10 +163,10 @@ int apex_attn_prefill(const void* q, const void* k, const void* v, void* o, void
     const long long blocks = (long long)p.n_pos_tiles * p.n_groups;
     if (blocks > 0x7fffffffLL) return APEX_EUNSUPPORTED;
     if (d_h == 128)
-      hipLaunchKernelGGL(apex::prefill_bf16_kernel<128>, dim3((unsigned)blocks),
+      hipLaunchKernelGGL((apex::prefill_bf16_kernel<128, 128, 128>), dim3((unsigned)blocks),
                          dim3(apex::kPfThreads), 0, st, p);
     else
-      hipLaunchKernelGGL(apex::prefill_bf16_kernel<64>, dim3((unsigned)blocks),
+      hipLaunchKernelGGL((apex::prefill_bf16_kernel<64, 64, 64>), dim3((unsigned)blocks),
                          dim3(apex::kPfThreads), 0, st, p);
   } else {
     apex::PrefillF32Params p{};
@@ -183,6 +185,54 @@ int apex_attn_prefill(const void* q, const void* k, const void* v, void* o, void
     else
       hipLaunchKernelGGL(apex::prefill_f32_kernel<64>, grid, dim3(apex::kF32Threads), 0, st, p);
   }
+  return launch_status();
+}
+
+int apex_attn_prefill_mla(const void* q, const void* k, const void* v, void* o,
+                          void* k_rope_out, int B, int S, int H_q, int H_kv, int d_h, int d_r,
+                          int causal, int W, int prefix, int64_t m0, double base, double yarn_s,
+                          int apply_rope, int dtype, void* stream) {
+  if (!q || !k || !v || !o || (apply_rope == 1 && !k_rope_out)) return APEX_EINVAL;
+  if (B < 1 || S < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0) return APEX_EINVAL;
+  if (d_h < 2 || (d_h & 1) || d_r < 2 || (d_r & 1)) return APEX_EINVAL;
+  if (W < 0 || (W > 0 && !causal) || (causal != 0 && causal != 1)) return APEX_EINVAL;
+  if (prefix < 0 || (prefix > 0 && !causal)) return APEX_EINVAL;
+  if (m0 < 0 || apply_rope < 0 || apply_rope > 2 || (apply_rope && !(base > 0.0)) ||
+      !yarn_ok(yarn_s))
+    return APEX_EINVAL;
+  if (dtype != APEX_F32 && dtype != APEX_BF16) return APEX_EINVAL;
+  if (dtype != APEX_BF16 || d_h != 128 || d_r != 64) return APEX_EUNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+
+  const int dqk = d_h + d_r;
+  const void* kr = k;
+  if (apply_rope == 1) {
+    const int rc = launch_rope(k, k_rope_out, (long long)B * H_kv, S, d_r, dqk, m0, base, yarn_s,
+                               dtype, st);
+    if (rc != APEX_OK) return rc;
+    kr = k_rope_out;
+  }
+  const int G = H_q / H_kv;
+  apex::PrefillParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)kr;
+  p.v = (const uint16_t*)v;
+  p.o = (uint16_t*)o;
+  p.S = S; p.Hq = H_q; p.Hkv = H_kv; p.G = G;
+  p.causal = causal; p.W = W; p.P = prefix < S ? prefix : S;
+  p.m0 = m0; p.base = base; p.yarn_s = yarn_s; p.apply_rope = apply_rope != 0;
+  p.g_pack = head_pack(G);
+  p.bm = apex::kPfRows / p.g_pack;
+  p.n_pos_tiles = (S + p.bm - 1) / p.bm;
+  p.n_head_packs = G / p.g_pack;
+  p.n_groups = B * H_kv * p.n_head_packs;
+  // scores are q.k over the whole [content | rope] width
+  p.sc = (float)(kLog2e * yarn_attn_factor(yarn_s) / sqrt((double)dqk));
+  const long long blocks = (long long)p.n_pos_tiles * p.n_groups;
+  if (blocks > 0x7fffffffLL) return APEX_EUNSUPPORTED;
+  hipLaunchKernelGGL((apex::prefill_bf16_kernel<192, 128, 64>), dim3((unsigned)blocks),
+                     dim3(apex::kPfThreads), 0, st, p);
   return launch_status();
 }
 

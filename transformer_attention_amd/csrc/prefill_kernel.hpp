@@ -72,11 +72,17 @@ struct PrefillParams {
   float sc;           // log2(e) / sqrt(d_h)
 };
 
-// Physical 16-byte chunk of logical chunk c in LDS row r.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);  // 16 chunks per row
-  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);           // 8 chunks per row
+// Physical 16-byte slot of logical chunk c in LDS row r of CPR chunks (and,
+// being an involution, the logical chunk held in slot c). For 8 and 16 chunks
+// the chunk index is XORed with row bits; for 24 chunks (a 192-wide row) the
+// low three bits are, inside each group of eight. Either way the 16 rows that
+// one K read touches with the same chunk land in 16 distinct bank groups.
+template <int CPR>
+__device__ __forceinline__ int slot(int c, int r) {
+  static_assert(CPR == 8 || CPR == 16 || CPR == 24, "row width");
+  if (CPR == 16) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  if (CPR == 8) return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  return (c & ~7) | ((c & 7) ^ ((r >> 1) & 7));
 }
 
 // True when every key of [j0, j0 + kPfBN) is visible to every row of
@@ -88,24 +94,34 @@ __device__ __forceinline__ int swz(int r) {
 __device__ __forceinline__ bool tile_is_full(int j0, int r0, int S, int causal, int W, int P) {
   const int j1 = j0 + kPfBN - 1;
   const int min_hi = r0 < P ? P - 1 : r0;
-  const int max_lo = (W > 0) & (r0 + 31 >= P) ? r0 + 32 - W : 0;
+  const int max_lo = ((W > 0) & (r0 + 31 >= P)) ? r0 + 32 - W : 0;
   return (j1 < S) & ((causal == 0) | ((j1 <= min_hi) & (j0 >= max_lo)));
 }
 
-template <int D>
+// DQK: width of the q and k rows; DV: width of the v and o rows; DR: the
+// last DR dims of q and k carry RoPE (DQK = DV = DR = d_h for the standard
+// layers; DQK = d_h + d_r, DV = d_h, DR = d_r for MLA with decoupled RoPE,
+// Part 2, §9.3).
+template <int DQK, int DV, int DR>
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillParams p) {
-  static_assert(D == 64 || D == 128, "head size");
-  constexpr int RB = D * 2;                       // bytes per LDS row
-  constexpr int TILE = kPfBN * RB;                // bytes per K or V tile
-  constexpr int LOADS = TILE / 1024 / kPfWaves;   // 1 KB direct loads per wave per tile
-  constexpr int ROWS_PER_LOAD = 1024 / RB;
-  constexpr int KK = D / 16;                      // MFMA steps over the head dimension
-  constexpr int DB = D / 32;                      // 32-wide blocks of the head dimension
-  static_assert(LOADS >= 1, "tile split");
+  static_assert(DQK % 16 == 0 && DV % 32 == 0 && DR % 16 == 0 && DR <= DQK, "head size");
+  constexpr int RBK = DQK * 2, RBV = DV * 2;       // bytes per LDS row of K, V
+  constexpr int CPRK = RBK / 16, CPRV = RBV / 16;  // 16-byte chunks per row
+  constexpr int TILEK = kPfBN * RBK;               // bytes per K tile
+  constexpr int TILEV = kPfBN * RBV;               // bytes per V tile
+  constexpr int LOADSK = TILEK / 1024 / kPfWaves;  // 1 KB direct loads per wave per tile
+  constexpr int LOADSV = TILEV / 1024 / kPfWaves;
+  constexpr int KK = DQK / 16;                     // MFMA steps over the q.k width
+  constexpr int KR = (DQK - DR) / 16;              // first step of the RoPE part
+  constexpr int DB = DV / 32;                      // 32-wide blocks of the v width
+  static_assert(LOADSK * kPfWaves * 1024 == TILEK && LOADSV * kPfWaves * 1024 == TILEV,
+                "tile split");
 
-  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[2][TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char vbuf[2][TILE];
-  __shared__ double turns_lds[D / 2];
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[2][TILEK];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf[2][TILEV];
+  // The RoPE turns are needed only while Q loads, before V slot 1 first
+  // receives a tile (after the prologue's second barrier): they borrow it.
+  double* const turns_lds = (double*)vbuf[1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -135,50 +151,64 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
   }
   const int t_lo = j_lo / kPfBN, t_hi = j_hi / kPfBN;
 
-  const uint16_t* kg = p.k + ((size_t)b * p.Hkv + kvh) * p.S * D;
-  const uint16_t* vg = p.v + ((size_t)b * p.Hkv + kvh) * p.S * D;
+  const uint16_t* kg = p.k + ((size_t)b * p.Hkv + kvh) * p.S * DQK;
+  const uint16_t* vg = p.v + ((size_t)b * p.Hkv + kvh) * p.S * DV;
 
   // ---- direct HBM -> LDS tile loads: lane order = physical LDS order ----
-  // Byte offset inside a tile of the 16 bytes each lane copies per load.
-  uint32_t ld_off[LOADS];
+  // Byte offset inside a tile of the 16 bytes each lane copies per load: the
+  // lane fills physical slot pc of the tile, which holds logical chunk
+  // slot(pc % CPR, row) of row pc / CPR.
+  uint32_t ldk_off[LOADSK], ldv_off[LOADSV];
 #pragma unroll
-  for (int i = 0; i < LOADS; i++) {
-    const int blk = wave + i * kPfWaves;                  // 1 KB block of the tile
-    const int r = blk * ROWS_PER_LOAD + lane / (RB / 16);
-    const int pc = lane % (RB / 16);
-    ld_off[i] = (uint32_t)(r * RB + ((pc ^ swz<D>(r)) << 4));  // logical chunk of the row
+  for (int i = 0; i < LOADSK; i++) {
+    const int pc = (wave + i * kPfWaves) * 64 + lane;
+    const int r = pc / CPRK;
+    ldk_off[i] = (uint32_t)(r * RBK + (slot<CPRK>(pc % CPRK, r) << 4));
+  }
+#pragma unroll
+  for (int i = 0; i < LOADSV; i++) {
+    const int pc = (wave + i * kPfWaves) * 64 + lane;
+    const int r = pc / CPRV;
+    ldv_off[i] = (uint32_t)(r * RBV + (slot<CPRV>(pc % CPRV, r) << 4));
   }
   // The buffer resource of tile t covers the rows t*kPfBN .. S-1, so rows
   // past the sequence end arrive as zeros (and are masked anyway).
-  auto issue_tile = [&](const uint16_t* src, unsigned char* dst, int t) {
+  auto issue_k = [&](unsigned char* dst, int t) {
     const buffer_rsrc r =
-        make_buffer_rsrc(src + (size_t)t * kPfBN * D, (uint32_t)(p.S - t * kPfBN) * RB);
+        make_buffer_rsrc(kg + (size_t)t * kPfBN * DQK, (uint32_t)(p.S - t * kPfBN) * RBK);
 #pragma unroll
-    for (int i = 0; i < LOADS; i++)
-      buffer_to_lds16(r, ld_off[i], (APEX_LDS void*)(dst + (wave + i * kPfWaves) * 1024));
+    for (int i = 0; i < LOADSK; i++)
+      buffer_to_lds16(r, ldk_off[i], (APEX_LDS void*)(dst + (wave + i * kPfWaves) * 1024));
+  };
+  auto issue_v = [&](unsigned char* dst, int t) {
+    const buffer_rsrc r =
+        make_buffer_rsrc(vg + (size_t)t * kPfBN * DV, (uint32_t)(p.S - t * kPfBN) * RBV);
+#pragma unroll
+    for (int i = 0; i < LOADSV; i++)
+      buffer_to_lds16(r, ldv_off[i], (APEX_LDS void*)(dst + (wave + i * kPfWaves) * 1024));
   };
 
-  issue_tile(kg, kbuf[0], t_lo);
-  issue_tile(vg, vbuf[0], t_lo);
-  if (t_lo < t_hi) issue_tile(kg, kbuf[1], t_lo + 1);
+  issue_k(kbuf[0], t_lo);
+  issue_v(vbuf[0], t_lo);
+  if (t_lo < t_hi) issue_k(kbuf[1], t_lo + 1);
 
-  if (p.apply_rope && tid < D / 2) turns_lds[tid] = rope_turns(tid, D, p.base, p.yarn_s);
+  if (p.apply_rope && tid < DR / 2) turns_lds[tid] = rope_turns(tid, DR, p.base, p.yarn_s);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's tile loads have landed
   __syncthreads();                                    // ... and every other wave's
 
   // ---- Q^T operand: lane holds row `row`, dims 16kk + 8g .. +7 ----
   u32x4 qf[KK];
   {
-    const uint16_t* qrow = p.q + (((size_t)b * p.Hq + head) * p.S + row) * D;
+    const uint16_t* qrow = p.q + (((size_t)b * p.Hq + head) * p.S + row) * DQK;
 #pragma unroll
     for (int kk = 0; kk < KK; kk++) {
       const int d0 = 16 * kk + 8 * g;
       u32x4 w = row < p.S ? *(const u32x4*)(qrow + d0) : u32x4{0, 0, 0, 0};
-      if (p.apply_rope) {
+      if (kk >= KR && p.apply_rope) {  // the RoPE part: pairs of a DR-wide head
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           float c, s;
-          rope_cs_fast(p.m0 + row, turns_lds[d0 / 2 + e], c, s);
+          rope_cs_fast(p.m0 + row, turns_lds[(d0 - (DQK - DR)) / 2 + e], c, s);
           const float x0 = bf16_lo(w[e]), x1 = bf16_hi(w[e]);
           w[e] = pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
         }
@@ -190,11 +220,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
   // ---- per-lane LDS offsets (loop invariant) ----
   // K operand: row kb*32 + r32, logical chunk 2kk + g.
   int k_off[KK];
-  {
-    const int sw = swz<D>(r32);
 #pragma unroll
-    for (int kk = 0; kk < KK; kk++) k_off[kk] = r32 * RB + (((2 * kk + g) ^ sw) << 4);
-  }
+  for (int kk = 0; kk < KK; kk++) k_off[kk] = r32 * RBK + (slot<CPRK>(2 * kk + g, r32) << 4);
   // V^T operand via ds_read_b64_tr_b16: lane j16 of 16-lane group qg reads 8 bytes
   // at row key + j16/4, columns 32db + 16(qg&1) + 4(j16&3): logical chunk
   // 4db + 2(qg&1) + (j16&3)/2, half (j16&1). Rows +8 give the k-indices 4..7.
@@ -204,11 +231,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
 #pragma unroll
   for (int h = 0; h < 2; h++) {
     const int r = vrow + 8 * h;
-    const int sw = swz<D>(r);
 #pragma unroll
     for (int db = 0; db < DB; db++) {
       const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1);
-      v_off[h][db] = r * RB + ((chunk ^ sw) << 4) + ((j16 & 1) << 3);
+      v_off[h][db] = r * RBV + (slot<CPRV>(chunk, r) << 4) + ((j16 & 1) << 3);
     }
   }
 
@@ -218,7 +244,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
       s[kb] = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < KK; kk++)
-        s[kb] = mfma32(*(const u32x4*)(kb_lds + kb * 32 * RB + k_off[kk]), qf[kk], s[kb]);
+        s[kb] = mfma32(*(const u32x4*)(kb_lds + kb * 32 * RBK + k_off[kk]), qf[kk], s[kb]);
     }
   };
 
@@ -242,8 +268,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
   auto step = [&](int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2], bool& full_cur,
                   bool& full_next) {
     const int it = t - t_lo;
-    if (t + 1 <= t_hi) issue_tile(vg, vbuf[(it + 1) & 1], t + 1);
-    if (t + 2 <= t_hi) issue_tile(kg, kbuf[it & 1], t + 2);
+    if (t + 1 <= t_hi) issue_v(vbuf[(it + 1) & 1], t + 1);
+    if (t + 2 <= t_hi) issue_k(kbuf[it & 1], t + 2);
 
     if (!full_cur) {  // per-element mask of tile t
       const int base = t * kPfBN + 4 * g - vis_lo;
@@ -306,7 +332,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
       for (int kb = 0; kb < 2; kb++)
 #pragma unroll
         for (int c = 0; c < 2; c++) {
-          const int koff = (kb * 32 + 16 * c) * RB;
+          const int koff = (kb * 32 + 16 * c) * RBV;
           const u32x2 lo = lds_read_tr16((const uint16_t*)(vb + koff + v_off[0][db]));
           const u32x2 hi = lds_read_tr16((const uint16_t*)(vb + koff + v_off[1][db]));
           oacc[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pk[kb][c], oacc[db]);
@@ -325,7 +351,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (row < p.S) {
     const float inv = 1.0f / l_tot;
-    uint16_t* orow = p.o + (((size_t)b * p.Hq + head) * p.S + row) * D;
+    uint16_t* orow = p.o + (((size_t)b * p.Hq + head) * p.S + row) * DV;
 #pragma unroll
     for (int db = 0; db < DB; db++)
 #pragma unroll

@@ -10,6 +10,11 @@
 // taken from a per-block table, then stores the rows. Consecutive threads
 // cover consecutive chunks of a row, so a wave reads and writes whole rows
 // (coalesced 16- or 32-byte accesses).
+//
+// A row may be wider than the rotated part: with MLA's decoupled RoPE (Part 2,
+// §9.3) only the last d_r dims of each [content | rope] row turn, with the
+// frequencies of a d_r-wide head. The other chunks are copied when the output
+// is a separate buffer and left alone in place.
 #pragma once
 #include "device_common.hpp"
 
@@ -23,7 +28,8 @@ struct RopeParams {
   void* dst;           // may equal src
   long long n_bh;      // B * H
   int S;
-  int d_h;
+  int d_h;             // width of the rotated part (its frequencies follow d_h)
+  int row_len;         // elements per row, >= d_h; the rotated part is the last d_h
   long long m0;
   double base;
   double yarn_s;      // YaRN scale factor (1 = plain RoPE)
@@ -72,41 +78,48 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeParams p) {
     rope_cs_accurate(1, turns, step_c[threadIdx.x], step_s[threadIdx.x]);
   }
   __syncthreads();
-  const int chunks = p.d_h >> 3;
+  // Chunks of 8 visited per row: the whole row out of place, the rotated part
+  // in place; chunk index rc0 is the first rotated one.
+  const int rc0 = (p.row_len - p.d_h) >> 3;
+  const int first = p.src == p.dst ? rc0 : 0;
+  const int chunks = (p.row_len >> 3) - first;
   const int row_blocks = (p.S + kRopeRows - 1) / kRopeRows;
   const long long total = p.n_bh * row_blocks * chunks;
   for (long long t = blockIdx.x * (long long)kRopeThreads + threadIdx.x; t < total;
        t += (long long)gridDim.x * kRopeThreads) {
-    const int ch = (int)(t % chunks);
+    const int ch = first + (int)(t % chunks);
     const long long rb_all = t / chunks;
     const int rb = (int)(rb_all % row_blocks);
     const long long bh = rb_all / row_blocks;
     const int s0 = rb * kRopeRows;
     const int rows = min(kRopeRows, p.S - s0);
-    const size_t off0 = ((size_t)bh * p.S + s0) * p.d_h + ch * 8;
+    const size_t off0 = ((size_t)bh * p.S + s0) * p.row_len + ch * 8;
     float x[kRopeRows][8];
 #pragma unroll
     for (int r = 0; r < kRopeRows; r++)
-      if (r < rows) RopeIO<T>::load(p.src, off0 + (size_t)r * p.d_h, x[r]);
-    float c[4], s[4];
+      if (r < rows) RopeIO<T>::load(p.src, off0 + (size_t)r * p.row_len, x[r]);
+    if (ch >= rc0) {
+      const int pi = (ch - rc0) * 4;  // first pair of this chunk in the rotated part
+      float c[4], s[4];
 #pragma unroll
-    for (int e = 0; e < 4; e++) rope_cs_accurate(p.m0 + s0, turns_lds[ch * 4 + e], c[e], s[e]);
+      for (int e = 0; e < 4; e++) rope_cs_accurate(p.m0 + s0, turns_lds[pi + e], c[e], s[e]);
 #pragma unroll
-    for (int r = 0; r < kRopeRows; r++) {
+      for (int r = 0; r < kRopeRows; r++) {
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const float a = x[r][2 * e], b = x[r][2 * e + 1];
-        x[r][2 * e] = a * c[e] - b * s[e];
-        x[r][2 * e + 1] = a * s[e] + b * c[e];
-        const float cs = step_c[ch * 4 + e], ss = step_s[ch * 4 + e];
-        const float cn = c[e] * cs - s[e] * ss;
-        s[e] = c[e] * ss + s[e] * cs;
-        c[e] = cn;
+        for (int e = 0; e < 4; e++) {
+          const float a = x[r][2 * e], b = x[r][2 * e + 1];
+          x[r][2 * e] = a * c[e] - b * s[e];
+          x[r][2 * e + 1] = a * s[e] + b * c[e];
+          const float cs = step_c[pi + e], ss = step_s[pi + e];
+          const float cn = c[e] * cs - s[e] * ss;
+          s[e] = c[e] * ss + s[e] * cs;
+          c[e] = cn;
+        }
       }
     }
 #pragma unroll
     for (int r = 0; r < kRopeRows; r++)
-      if (r < rows) RopeIO<T>::store(p.dst, off0 + (size_t)r * p.d_h, x[r]);
+      if (r < rows) RopeIO<T>::store(p.dst, off0 + (size_t)r * p.row_len, x[r]);
   }
 }
 
