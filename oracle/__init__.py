@@ -55,6 +55,8 @@ def lib():
                                               i32, i64, i64, dbl, dbl, i32, i64, vp, vp, vp, i32]
         L.apex_oracle_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                          i64, dbl, dbl, i32, i64, vp, vp, i32]
+        L.apex_oracle_decode_mla.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                             i32, i32, i64, dbl, dbl, i32, i64, vp, vp, i32]
         _lib = L
     return _lib
 
@@ -187,6 +189,36 @@ def decode(q, k_cache, v_cache, k_new, v_new, m, W=0, base=10000.0, apply_rope=T
         raise ValueError("apex_oracle_decode rejected its arguments")
     return out.reshape(B, Hq, 1, d) if rows is None else out
 
+
+
+def decode_mla(q, k_cache, v_cache, k_new, v_new, m, d_r, W=0, base=10000.0, apply_rope=True,
+               rows=None, nthreads=None, yarn_s=1.0):
+    """MLA decode: q [B,Hq,1,d_h+d_r] at position m; k_cache [B,Hkv,Sk,d_h+d_r],
+    v_cache [B,Hkv,Sk,d_h]; k_new [B,Hkv,1,d_h+d_r], v_new [B,Hkv,1,d_h] or None.
+    RoPE on the last d_r dims of q and k_new. Returns fp64 [len(rows), d_h] or
+    [B,Hq,1,d_h]."""
+    qa, dt = _as_input(q)
+    kc, _ = _as_input(k_cache)
+    vc, _ = _as_input(v_cache)
+    kn = _as_input(k_new)[0] if k_new is not None else None
+    vn = _as_input(v_new)[0] if v_new is not None else None
+    B, Hq, _, dqk = qa.shape
+    Hkv, Sk, d_h = kc.shape[1], kc.shape[2], vc.shape[3]
+    if dqk != d_h + d_r or kc.shape[3] != dqk:
+        raise ValueError("shape mismatch")
+    if rows is None:
+        nrows, rarr = B * Hq, None
+    else:
+        rarr = np.ascontiguousarray(rows, np.int64)
+        nrows = rarr.size
+    out = np.empty((nrows, d_h), np.float64)
+    rc = lib().apex_oracle_decode_mla(_ptr(qa), _ptr(kc), _ptr(vc), _ptr(kn), _ptr(vn), dt,
+                                      B, Sk, Hq, Hkv, d_h, int(d_r), int(W), int(m), float(base),
+                                      float(yarn_s), int(apply_rope), nrows, _ptr(rarr),
+                                      _ptr(out), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("apex_oracle_decode_mla rejected its arguments")
+    return out.reshape(B, Hq, 1, d_h) if rows is None else out
 
 
 def rmsnorm(x, gamma, eps=1e-6, nthreads=None):

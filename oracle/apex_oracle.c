@@ -299,7 +299,7 @@ int apex_oracle_prefill_mla(const void* q, const void* k, const void* v, int dty
 /* ----------------------------- decode ----------------------------- */
 typedef struct {
   const void *q, *kc, *vc, *kn, *vn;
-  int dtype, Sk, Hq, Hkv, d, W, apply_rope;
+  int dtype, Sk, Hq, Hkv, d, dv, r_off, d_rope, W, apply_rope;
   int64_t m;
   double base, yarn_s;
   const int64_t* rows;  /* flat b*Hq + h */
@@ -308,11 +308,11 @@ typedef struct {
 
 static void decode_rows(void* p, int64_t lo, int64_t hi) {
   decode_ctx* c = (decode_ctx*)p;
-  int d = c->d, G = c->Hq / c->Hkv;
+  int d = c->d, dv = c->dv, G = c->Hq / c->Hkv;
   int64_t n_max = c->m + 1;
   double* q = (double*)malloc(sizeof(double) * d);
   double* kd = (double*)malloc(sizeof(double) * (size_t)n_max * d);
-  double* vd = (double*)malloc(sizeof(double) * (size_t)n_max * d);
+  double* vd = (double*)malloc(sizeof(double) * (size_t)n_max * dv);
   double* scores = (double*)malloc(sizeof(double) * n_max);
   const double** keys = (const double**)malloc(sizeof(double*) * n_max);
   const double** vals = (const double**)malloc(sizeof(double*) * n_max);
@@ -321,45 +321,52 @@ static void decode_rows(void* p, int64_t lo, int64_t hi) {
     int64_t bh = c->rows ? c->rows[r] : r;
     int64_t b = bh / c->Hq, h = bh % c->Hq, kvh = h / G;
     for (int t = 0; t < d; t++) q[t] = load_elem(c->q, c->dtype, bh * d + t);
-    if (c->apply_rope) apex_oracle_rope_row(q, q, d, c->m, c->base, c->yarn_s);
+    if (c->apply_rope)
+      apex_oracle_rope_row(q + c->r_off, q + c->r_off, c->d_rope, c->m, c->base, c->yarn_s);
     int64_t kv_row0 = (b * c->Hkv + kvh) * (int64_t)c->Sk;
     int64_t n = 0;
     for (int64_t j = 0; j <= c->m; j++) {
       if (!apex_oracle_visible(c->m, j, 1, c->W, 0)) continue;
       double* kr = kd + n * d;
-      double* vr = vd + n * d;
+      double* vr = vd + n * dv;
       if (j == c->m && c->kn) {
         for (int t = 0; t < d; t++) kr[t] = load_elem(c->kn, c->dtype, (b * c->Hkv + kvh) * d + t);
-        if (c->apply_rope) apex_oracle_rope_row(kr, kr, d, c->m, c->base, c->yarn_s);
+        if (c->apply_rope)
+          apex_oracle_rope_row(kr + c->r_off, kr + c->r_off, c->d_rope, c->m, c->base, c->yarn_s);
       } else {
         for (int t = 0; t < d; t++) kr[t] = load_elem(c->kc, c->dtype, (kv_row0 + j) * d + t);
       }
       if (j == c->m && c->vn) {
-        for (int t = 0; t < d; t++) vr[t] = load_elem(c->vn, c->dtype, (b * c->Hkv + kvh) * d + t);
+        for (int t = 0; t < dv; t++)
+          vr[t] = load_elem(c->vn, c->dtype, (b * c->Hkv + kvh) * dv + t);
       } else {
-        for (int t = 0; t < d; t++) vr[t] = load_elem(c->vc, c->dtype, (kv_row0 + j) * d + t);
+        for (int t = 0; t < dv; t++) vr[t] = load_elem(c->vc, c->dtype, (kv_row0 + j) * dv + t);
       }
       keys[n] = kr;
       vals[n] = vr;
       n++;
     }
-    attend(q, keys, vals, n, d, d, scale, scores, c->out + r * d, NULL);
+    attend(q, keys, vals, n, d, dv, scale, scores, c->out + r * dv, NULL);
   }
   free(q); free(kd); free(vd); free(scores); free(keys); free(vals);
 }
 
-/* Decode step: one query per (b, h) at position m against a cache of Sk slots.
- * q [B,Hq,1,d]; k_cache, v_cache [B,Hkv,Sk,d] (slots stored rotated);
- * k_new, v_new [B,Hkv,1,d] or NULL (then slot m is read from the cache).
- * rows: flat b*Hq+h, or NULL for all. out [nrows, d]. */
-int apex_oracle_decode(const void* q, const void* k_cache, const void* v_cache,
-                       const void* k_new, const void* v_new, int dtype,
-                       int B, int Sk, int Hq, int Hkv, int d, int W, int64_t m,
-                       double base, double yarn_s, int apply_rope,
-                       int64_t nrows, const int64_t* rows, double* out, int nthreads) {
+/* Decode step, general form: one query per (b, h) at position m against a
+ * cache of Sk slots. q [B,Hq,1,dqk]; k_cache [B,Hkv,Sk,dqk], v_cache
+ * [B,Hkv,Sk,dv] (slots stored rotated); k_new [B,Hkv,1,dqk], v_new
+ * [B,Hkv,1,dv] or NULL (then slot m is read from the cache). RoPE rotates
+ * dims [r_off, r_off + d_rope) of q and k_new with the frequencies of a
+ * d_rope-dimensional head; scores scaled by attn_factor(yarn_s) / sqrt(dqk).
+ * rows: flat b*Hq+h, or NULL for all. out [nrows, dv]. */
+static int decode_general(const void* q, const void* k_cache, const void* v_cache,
+                          const void* k_new, const void* v_new, int dtype, int B, int Sk, int Hq,
+                          int Hkv, int dqk, int dv, int r_off, int d_rope, int W, int64_t m,
+                          double base, double yarn_s, int apply_rope, int64_t nrows,
+                          const int64_t* rows, double* out, int nthreads) {
   if (!q || !k_cache || !v_cache || !out || B < 1 || Sk < 1 || Hq < 1 || Hkv < 1 ||
-      Hq % Hkv || d < 2 || (d & 1) || W < 0 || m < 0 || m >= Sk ||
-      (dtype != 0 && dtype != 1) || (apply_rope && !(base > 0.0)) || !(yarn_s >= 1.0))
+      Hq % Hkv || dqk < 1 || dv < 1 || d_rope < 2 || (d_rope & 1) || r_off < 0 ||
+      r_off + d_rope > dqk || W < 0 || m < 0 || m >= Sk || (dtype != 0 && dtype != 1) ||
+      (apply_rope && !(base > 0.0)) || !(yarn_s >= 1.0))
     return -1;
   int64_t total = (int64_t)B * Hq;
   if (!rows) nrows = total;
@@ -367,10 +374,34 @@ int apex_oracle_decode(const void* q, const void* k_cache, const void* v_cache,
     int64_t f = rows ? rows[r] : r;
     if (f < 0 || f >= total) return -1;
   }
-  decode_ctx c = {q, k_cache, v_cache, k_new, v_new, dtype, Sk, Hq, Hkv, d, W, apply_rope,
-                  m, base, yarn_s, rows, out};
+  decode_ctx c = {q, k_cache, v_cache, k_new, v_new, dtype, Sk, Hq, Hkv, dqk, dv, r_off, d_rope,
+                  W, apply_rope, m, base, yarn_s, rows, out};
   parallel_for(nrows, nthreads, decode_rows, &c);
   return 0;
+}
+
+/* Decode with q, k and v rows of d values and RoPE over the whole row. */
+int apex_oracle_decode(const void* q, const void* k_cache, const void* v_cache,
+                       const void* k_new, const void* v_new, int dtype,
+                       int B, int Sk, int Hq, int Hkv, int d, int W, int64_t m,
+                       double base, double yarn_s, int apply_rope,
+                       int64_t nrows, const int64_t* rows, double* out, int nthreads) {
+  if (d < 2 || (d & 1)) return -1;
+  return decode_general(q, k_cache, v_cache, k_new, v_new, dtype, B, Sk, Hq, Hkv, d, d, 0, d, W,
+                        m, base, yarn_s, apply_rope, nrows, rows, out, nthreads);
+}
+
+/* MLA decode with decoupled RoPE (Part 2, §9.3): q, k_cache, k_new rows of
+ * d_h + d_r values [content | rope], RoPE on the last d_r; v rows and out of
+ * d_h values; scale 1 / sqrt(d_h + d_r). */
+int apex_oracle_decode_mla(const void* q, const void* k_cache, const void* v_cache,
+                           const void* k_new, const void* v_new, int dtype,
+                           int B, int Sk, int Hq, int Hkv, int d_h, int d_r, int W, int64_t m,
+                           double base, double yarn_s, int apply_rope,
+                           int64_t nrows, const int64_t* rows, double* out, int nthreads) {
+  if (d_h < 1) return -1;
+  return decode_general(q, k_cache, v_cache, k_new, v_new, dtype, B, Sk, Hq, Hkv, d_h + d_r, d_h,
+                        d_h, d_r, W, m, base, yarn_s, apply_rope, nrows, rows, out, nthreads);
 }
 
 /* ----------------------------- RMSNorm ----------------------------- */

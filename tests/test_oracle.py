@@ -723,3 +723,39 @@ def test_mla_c_oracle_matches_python_twin():
     ref = np.array(pyref.prefill_mla(q.astype(float).tolist(), k.astype(float).tolist(),
                                      v.astype(float).tolist(), d_r, True, 3, 11, 10000.0, 2, 2.0))
     assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_mla_decode_equals_last_mla_prefill_row():
+    # the decode of the query at m = S - 1 against a cache of the S keys is the
+    # last row of the prefill, itself pinned to torch's SDPA above
+    B, Hq, Hkv, S, d_h, d_r = 1, 4, 2, 20, 16, 8
+    q = _rand((B, Hq, S, d_h + d_r))
+    k, v = _rand((B, Hkv, S, d_h + d_r)), _rand((B, Hkv, S, d_h))
+    for W in (0, 6):
+        pre = oracle.prefill_mla(q, k, v, d_r, causal=1, W=W, apply_rope=False)
+        dec = oracle.decode_mla(_f32(q[:, :, S - 1:]), k, v, None, None, m=S - 1, d_r=d_r, W=W,
+                                apply_rope=False)
+        assert np.array_equal(dec[:, :, 0], pre[:, :, S - 1])
+    # with RoPE: the cache holds [content | rotated rope part] keys, the new
+    # key arrives raw and only its rope part turns at m
+    krot = k.astype(np.float64).copy()
+    for h in range(Hkv):
+        for j in range(S):
+            krot[0, h, j, d_h:] = oracle.rope_row(k[0, h, j, d_h:], j)
+    pre = _torch_mla_reference(q, k, v, d_r, 0, 10000.0)
+    dec = oracle.decode_mla(_f32(q[:, :, S - 1:]), _f32(krot), v, _f32(k[:, :, S - 1:]),
+                            _f32(v[:, :, S - 1:]), m=S - 1, d_r=d_r)
+    assert np.max(np.abs(dec[:, :, 0] - pre[:, :, S - 1])) <= 1e-5
+
+
+def test_mla_decode_uses_new_key_value_at_slot_m():
+    B, Hq, Hkv, Sk, d_h, d_r = 1, 2, 1, 7, 8, 4
+    q = _rand((B, Hq, 1, d_h + d_r))
+    kc, vc = _rand((B, Hkv, Sk, d_h + d_r)), _rand((B, Hkv, Sk, d_h))
+    kn, vn = _rand((B, Hkv, 1, d_h + d_r)), _rand((B, Hkv, 1, d_h))
+    m = 4
+    got = oracle.decode_mla(q, kc, vc, kn, vn, m=m, d_r=d_r, apply_rope=False)
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[:, :, m], vc2[:, :, m] = kn[:, :, 0], vn[:, :, 0]
+    assert np.array_equal(got, oracle.decode_mla(q, kc2, vc2, None, None, m=m, d_r=d_r,
+                                                 apply_rope=False))
