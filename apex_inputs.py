@@ -50,6 +50,9 @@ WORKLOADS = {
                                    seed=9),
     "gqa_decode_sk32768": dict(kind="decode", B=64, Sk=32768, Hq=128, Hkv=8, d=128, W=0,
                                m=32767, base=10000.0, dtype="bf16", seed=5),
+    # MLA global-layer decode: the same batch and cache length with [content | rope] keys
+    "mla_global_decode_sk32768": dict(kind="mla_decode", B=64, Sk=32768, Hq=128, Hkv=8, d=128,
+                                      d_r=64, W=0, m=32767, base=10000.0, dtype="bf16", seed=13),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -102,6 +105,18 @@ def decode_inputs(B, Sk, Hq, Hkv, d, dtype="bf16", seed=0, device="cpu"):
     return q, k_cache, v_cache, k_new, v_new
 
 
+def mla_decode_inputs(B, Sk, Hq, Hkv, d, d_r, dtype="bf16", seed=0, device="cpu"):
+    """(q [B,Hq,1,d+d_r], k_cache [B,Hkv,Sk,d+d_r], v_cache [B,Hkv,Sk,d],
+    k_new [B,Hkv,1,d+d_r], v_new [B,Hkv,1,d]): [content | rope] keys."""
+    dt = TORCH_DTYPE[dtype] if isinstance(dtype, str) else dtype
+    q = normal((B, Hq, 1, d + d_r), seed * 16 + 0, dt, device)
+    k_new = normal((B, Hkv, 1, d + d_r), seed * 16 + 1, dt, device)
+    v_new = normal((B, Hkv, 1, d), seed * 16 + 2, dt, device)
+    k_cache = normal((B, Hkv, Sk, d + d_r), seed * 16 + 3, dt, device)
+    v_cache = normal((B, Hkv, Sk, d), seed * 16 + 4, dt, device)
+    return q, k_cache, v_cache, k_new, v_new
+
+
 def rmsnorm_inputs(B, S, d, dtype="bf16", seed=0, device="cpu"):
     """(x [B,S,d] ~ N(0,1), gamma [d] ~ 1 + 0.1 N(0,1)): gamma away from its
     initial all-ones value so that the scale is exercised."""
@@ -118,6 +133,9 @@ def workload_inputs(name, device="cpu"):
     if w["kind"] == "mla_prefill":
         return mla_prefill_inputs(w["B"], w["S"], w["Hq"], w["Hkv"], w["d"], w["d_r"], w["dtype"],
                                   w["seed"], device)
+    if w["kind"] == "mla_decode":
+        return mla_decode_inputs(w["B"], w["Sk"], w["Hq"], w["Hkv"], w["d"], w["d_r"], w["dtype"],
+                                 w["seed"], device)
     if w["kind"] == "prefill":
         return prefill_inputs(w["B"], w["S"], w["Hq"], w["Hkv"], w["d"], w["dtype"], w["seed"],
                               device)

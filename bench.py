@@ -31,6 +31,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 HEADLINE = "gqa_prefill_s2048"
 DECODE = "gqa_decode_sk32768"
+MLA_DECODE = "mla_global_decode_sk32768"
 RMSNORMS = ("rmsnorm_b4_s2048_d7168", "rmsnorm_b64_s2048_d512")
 OTHERS = ("window_prefill_s16384_w4096", "local_prefill_s65536_w512",
           "prefix_prefill_s2048_p512", "prefix_local_prefill_s16384_w4096_p1024",
@@ -78,9 +79,10 @@ def prefill_bytes(w):
 
 def decode_bytes(w):
     """Algorithmic bytes of one decode call: the K and V caches read once, q
-    read, o written, the new key and value read."""
+    read, o written, the new key and value read (keys d_h + d_r wide for MLA)."""
     B, Sk, Hq, Hkv, d = w["B"], w["Sk"], w["Hq"], w["Hkv"], w["d"]
-    return 2 * (2 * B * Hkv * Sk * d + 2 * B * Hq * d + 2 * B * Hkv * d)
+    dk = d + w.get("d_r", 0)
+    return 2 * ((B * Hkv * Sk + B * Hq + B * Hkv) * (dk + d))
 
 
 def rmsnorm_bytes(w):
@@ -173,19 +175,19 @@ def time_rmsnorm(taa, torch, name, steps, warmup):
     return w, sum(ms) / len(ms), ms[0]
 
 
-def time_decode(taa, torch, steps, warmup):
+def time_decode(taa, torch, steps, warmup, name=DECODE):
     import apex_inputs
-    w = apex_inputs.WORKLOADS[DECODE]
-    q, kc, vc, kn, vn = apex_inputs.workload_inputs(DECODE, device="cuda")
-    B, Hq, _, d = q.shape
-    Hkv, Sk = kc.shape[1], kc.shape[2]
-    o = torch.empty_like(q)
+    w = apex_inputs.WORKLOADS[name]
+    q, kc, vc, kn, vn = apex_inputs.workload_inputs(name, device="cuda")
+    B, Hq = q.shape[:2]
+    Hkv, Sk, d = kc.shape[1], kc.shape[2], w["d"]
+    o = torch.empty(B, Hq, 1, d, dtype=q.dtype, device="cuda")
     ws = torch.empty(taa.apex_attn_decode_workspace_bytes(B, Hq, Hkv, Sk, d), dtype=torch.uint8,
                      device="cuda")
+    fn = taa.apex_attn_decode_mla if w["kind"] == "mla_decode" else taa.apex_attn_decode
 
     def call():
-        taa.apex_attn_decode(q, kc, vc, kn, vn, o, m=w["m"], W=w["W"], base=w["base"],
-                             workspace=ws)
+        fn(q, kc, vc, kn, vn, o, m=w["m"], W=w["W"], base=w["base"], workspace=ws)
 
     for _ in range(warmup):
         call()
@@ -338,6 +340,18 @@ def main():
             "ms_median": round(d_med, 4), "ms_min": round(d_min, 4),
             "algorithmic_bytes": dbytes, "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
             "note": "whole call: split-K pass + combine pass, events on the launch stream"}
+        torch.cuda.empty_cache()
+        log("timing %s: %d warmup + %d calls" % (MLA_DECODE, args.warmup, dsteps))
+        mw, m_mean, m_med, m_min = time_decode(taa, torch, dsteps, args.warmup, MLA_DECODE)
+        mbytes = decode_bytes(mw)
+        mgbs = mbytes / (m_mean * 1e-3) / 1e9
+        log("mla decode %.4f ms -> %.1f GB/s" % (m_mean, mgbs))
+        extra["decode_mla"] = {
+            "workload": MLA_DECODE, "value": round(mgbs, 1), "unit": "GB/s",
+            "ms_per_call": round(m_mean, 4), "ms_median": round(m_med, 4),
+            "ms_min": round(m_min, 4), "algorithmic_bytes": mbytes,
+            "frac_of_hbm_peak": round(mgbs / PEAK_HBM_GBS, 4)}
+        torch.cuda.empty_cache()
         others = {}
         for name in OTHERS:
             log("timing %s" % name)

@@ -191,6 +191,33 @@ int apex_attn_decode(const void* q, void* k_cache, void* v_cache,
                      double base, double yarn_s, int apply_rope, void* workspace,
                      size_t workspace_bytes, int dtype, void* stream);
 
+/*
+ * apex_attn_decode_mla -- apex_attn_decode for MLA with decoupled RoPE
+ * (Part 2, §9.3): query and cached key rows are [content (d_h) | rope (d_r)],
+ * value rows and the output d_h wide; scores scaled by 1 / sqrt(d_h + d_r)
+ * (the reading taken for apex_attn_prefill_mla).
+ *   q: [B, H_q, 1, d_h + d_r] raw query; its rope part is rotated at m when
+ *     apply_rope = 1 (frequencies of a d_r-wide head, YaRN as for
+ *     apex_rope_qk), the content part is used as is.
+ *   k_cache: [B, H_kv, Sk, d_h + d_r], rope parts stored already rotated.
+ *   v_cache: [B, H_kv, Sk, d_h].
+ *   k_new: [B, H_kv, 1, d_h + d_r], v_new: [B, H_kv, 1, d_h], or both NULL;
+ *     when given they go to slot m as in apex_attn_decode (k_new's rope part
+ *     rotated first when apply_rope = 1).
+ *   o: [B, H_q, 1, d_h] output.
+ *   workspace: at least apex_attn_decode_workspace_bytes(B, H_q, H_kv, Sk, d_h)
+ *     bytes (the partial results are d_h wide).
+ *   W, m, base, yarn_s, apply_rope, dtype, stream: as for apex_attn_decode.
+ * Built for bf16 with d_h = 128, d_r = 64.
+ * Errors: as apex_attn_decode, with d_h and d_r each even and >= 2
+ * (APEX_EINVAL otherwise); APEX_EUNSUPPORTED for any other (d_h, d_r) or fp32.
+ */
+int apex_attn_decode_mla(const void* q, void* k_cache, void* v_cache,
+                         const void* k_new, const void* v_new, void* o,
+                         int B, int Sk, int H_q, int H_kv, int d_h, int d_r, int W,
+                         int64_t m, double base, double yarn_s, int apply_rope,
+                         void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
 /* apex_strerror -- static text for a status code; never NULL. */
 const char* apex_strerror(int status);
 

@@ -29,8 +29,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["apex_attn_decode", "apex_attn_decode_workspace_bytes",
-                                    "apex_attn_prefill", "apex_attn_prefill_mla", "apex_rmsnorm",
+    assert declared_functions() == ["apex_attn_decode", "apex_attn_decode_mla",
+                                    "apex_attn_decode_workspace_bytes", "apex_attn_prefill", "apex_attn_prefill_mla", "apex_rmsnorm",
                                     "apex_rope_qk", "apex_strerror"]
 
 
@@ -181,6 +181,35 @@ def test_decode_rejects(L):
     assert _decode(L, dtype=0) == EUNSUP    # decode is built for bf16 caches
     assert _decode(L, ws=None) == EWS
     assert _decode(L, wsb=16) == EWS
+
+
+def _decode_mla(L, q=P, kc=P, vc=P, kn=P, vn=P, o=P, B=2, Sk=64, Hq=16, Hkv=1, d=128, dr=64,
+                W=0, m=63, base=1e4, yarn=1.0, rope=1, ws=P, wsb=None, dtype=1):
+    if wsb is None:
+        wsb = L.apex_attn_decode_workspace_bytes(B, Hq, Hkv, Sk, d) if Hkv > 0 else 0
+    return L.apex_attn_decode_mla(q, kc, vc, kn, vn, o, B, Sk, Hq, Hkv, d, dr, W, m, base, yarn,
+                                  rope, ws, wsb, dtype, None)
+
+
+def test_decode_mla_rejects(L):
+    for kw in (dict(q=None), dict(kc=None), dict(vc=None), dict(o=None)):
+        assert _decode_mla(L, **kw) == EINVAL, kw
+    assert _decode_mla(L, kn=None) == EINVAL
+    assert _decode_mla(L, Hq=12, Hkv=8) == EINVAL
+    assert _decode_mla(L, B=0) == EINVAL
+    assert _decode_mla(L, W=-1) == EINVAL
+    assert _decode_mla(L, m=64) == EINVAL
+    assert _decode_mla(L, base=0.0) == EINVAL
+    assert _decode_mla(L, yarn=0.5) == EINVAL
+    assert _decode_mla(L, rope=2) == EINVAL
+    assert _decode_mla(L, dtype=4) == EINVAL
+    assert _decode_mla(L, d=127) == EINVAL
+    assert _decode_mla(L, dr=1) == EINVAL
+    assert _decode_mla(L, d=64) == EUNSUP     # built for d_h = 128, d_r = 64, bf16
+    assert _decode_mla(L, dr=32) == EUNSUP
+    assert _decode_mla(L, dtype=0) == EUNSUP
+    assert _decode_mla(L, ws=None) == EWS
+    assert _decode_mla(L, wsb=64) == EWS
 
 
 def _rms(L, x=P, g=P, y=P, rows=4, d=64, eps=1e-6, dtype=1):

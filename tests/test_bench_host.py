@@ -34,6 +34,9 @@ def test_workload_counts():
     assert bench.n_visible(65536, 1, 512) == 33423616
     assert bench.prefill_flops(w["gqa_prefill_s2048"]) == 137506062336
     assert bench.decode_bytes(w["gqa_decode_sk32768"]) == 8594391040
+    # MLA decode: 192-wide keys, 128-wide values
+    assert bench.decode_bytes(w["mla_global_decode_sk32768"]) == \
+        2 * (64 * 8 * 32768 + 64 * 128 + 64 * 8) * (192 + 128)
     # MLA: q.k over 128 + 64 dims, p.v over 128 -> 2 * 320 FLOPs per pair and head
     assert bench.prefill_flops(w["mla_global_prefill_s16384"]) == 640 * 64 * (16384 * 16385 // 2)
     assert bench.prefill_bytes(w["mla_global_prefill_s16384"]) == 2 * 16384 * 72 * 320

@@ -460,6 +460,94 @@ def test_workload_gqa_decode_sk32768(taa):
         _check(o[b:b + 1], ref, "bf16", "%s batch %d (all %d heads)" % (name, b, Hq))
 
 
+# ----------------------------------------------------------- MLA decode ----
+MLA_DECODE_CASES = [
+    # B, Sk, Hq, Hkv, W, m, with_new, apply_rope, yarn_s -- d_h 128, d_r 64
+    (1, 1, 16, 1, 0, 0, True, 1, 1.0),
+    (2, 40, 8, 2, 0, 39, True, 1, 1.0),
+    (1, 1000, 32, 8, 100, 999, False, 0, 1.0),
+    (2, 5000, 64, 4, 0, 3210, True, 1, 1.0),
+    (1, 3000, 16, 2, 0, 2999, True, 1, 8.0),
+]
+
+
+@pytest.mark.parametrize("case", MLA_DECODE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_decode_mla(taa, case):
+    B, Sk, Hq, Hkv, W, m, with_new, rope, ys = case
+    _say("decode mla", case)
+    q, kc, vc, kn, vn = apex_inputs.mla_decode_inputs(B, Sk, Hq, Hkv, 128, 64, "bf16",
+                                                      seed=Sk + Hq + 2, device="cuda")
+    if not with_new:
+        kn = vn = None
+    kc0, vc0 = kc.cpu(), vc.cpu()
+    o = torch.empty(B, Hq, 1, 128, dtype=q.dtype, device="cuda")
+    ws = torch.empty(taa.apex_attn_decode_workspace_bytes(B, Hq, Hkv, Sk, 128),
+                     dtype=torch.uint8, device="cuda")
+    taa.apex_attn_decode_mla(q, kc, vc, kn, vn, o, m=m, W=W, apply_rope=rope, workspace=ws,
+                             yarn_s=ys)
+    torch.cuda.synchronize()
+    ref = oracle.decode_mla(q.cpu(), kc0, vc0, kn.cpu() if with_new else None,
+                            vn.cpu() if with_new else None, m=m, d_r=64, W=W, apply_rope=rope,
+                            yarn_s=ys)
+    _check(o, ref, "bf16", "decode mla %s" % (case,))
+    kc1, vc1 = kc.cpu(), vc.cpu()
+    other = torch.ones(Sk, dtype=torch.bool)
+    other[m] = False
+    assert torch.equal(kc1[:, :, other], kc0[:, :, other])  # only slot m may change
+    assert torch.equal(vc1[:, :, other], vc0[:, :, other])
+    if with_new:
+        assert torch.equal(vc1[:, :, m], vn.cpu()[:, :, 0])
+        x = kn.cpu().double().numpy()[:, :, 0]
+        got = kc1[:, :, m].double().numpy()
+        assert np.array_equal(got[..., :128], x[..., :128])  # content part stored as given
+        want = np.array([[oracle.rope_row(x[b, h, 128:], m, yarn_s=ys) if rope else x[b, h, 128:]
+                          for h in range(Hkv)] for b in range(B)])
+        assert np.all(np.abs(got[..., 128:] - want) <= np.abs(want) * 2.0 ** -8 + 1e-6)
+
+
+def test_decode_mla_equals_last_mla_prefill_row(taa):
+    B, S, Hq, Hkv = 1, 1200, 32, 4
+    q, k, v = apex_inputs.mla_prefill_inputs(B, S, Hq, Hkv, 128, 64, "bf16", seed=14,
+                                             device="cuda")
+    o = torch.empty(B, Hq, S, 128, dtype=q.dtype, device="cuda")
+    kr = torch.empty_like(k)
+    taa.apex_attn_prefill_mla(q, k, v, o, kr)
+    kc, vc = kr.clone(), v.clone()
+    kc[:, :, S - 1].zero_()  # slot m comes from k_new / v_new
+    vc[:, :, S - 1].zero_()
+    od = torch.empty(B, Hq, 1, 128, dtype=q.dtype, device=q.device)
+    ws = torch.empty(taa.apex_attn_decode_workspace_bytes(B, Hq, Hkv, S, 128), dtype=torch.uint8,
+                     device="cuda")
+    taa.apex_attn_decode_mla(q[:, :, S - 1:].contiguous(), kc, vc, k[:, :, S - 1:].contiguous(),
+                             v[:, :, S - 1:].contiguous(), od, m=S - 1, workspace=ws)
+    torch.cuda.synchronize()
+    diff = (od[:, :, 0].float() - o[:, :, S - 1].float()).abs().max().item()
+    _say("mla decode vs prefill last row: max_abs %.3g" % diff)
+    assert diff <= 2e-2
+
+
+def test_workload_mla_global_decode_sk32768(taa):
+    name = "mla_global_decode_sk32768"
+    w = apex_inputs.WORKLOADS[name]
+    _say("workload", name, w)
+    q, kc, vc, kn, vn = apex_inputs.workload_inputs(name, device="cuda")
+    B, Hq = q.shape[:2]
+    Hkv, Sk = kc.shape[1], kc.shape[2]
+    bs = [0, 29, B - 1]
+    saved = [(kc[b].cpu(), vc[b].cpu()) for b in bs]
+    o = torch.empty(B, Hq, 1, w["d"], dtype=q.dtype, device="cuda")
+    ws = torch.empty(taa.apex_attn_decode_workspace_bytes(B, Hq, Hkv, Sk, w["d"]),
+                     dtype=torch.uint8, device="cuda")
+    taa.apex_attn_decode_mla(q, kc, vc, kn, vn, o, m=w["m"], W=w["W"], base=w["base"],
+                             workspace=ws)
+    torch.cuda.synchronize()
+    for b, (kcb, vcb) in zip(bs, saved):
+        ref = oracle.decode_mla(q[b:b + 1].cpu(), kcb[None], vcb[None], kn[b:b + 1].cpu(),
+                                vn[b:b + 1].cpu(), m=w["m"], d_r=w["d_r"], W=w["W"],
+                                base=w["base"])
+        _check(o[b:b + 1], ref, "bf16", "%s batch %d (all %d heads)" % (name, b, Hq))
+
+
 # -------------------------------------------------------------- RMSNorm ----
 def _check_rmsnorm(got, ref, dtype, what):
     got = got.detach().to("cpu", torch.float64).numpy().reshape(ref.shape)

@@ -51,6 +51,9 @@ def lib():
         L.apex_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
                                        dbl, dbl, i32, vp, sz, i32, vp]
         L.apex_attn_decode.restype = i32
+        L.apex_attn_decode_mla.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                           i32, i64, dbl, dbl, i32, vp, sz, i32, vp]
+        L.apex_attn_decode_mla.restype = i32
         L.apex_strerror.argtypes = [i32]
         L.apex_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -163,3 +166,18 @@ def apex_attn_decode(q, k_cache, v_cache, k_new, v_new, o, m, W=0, base=10000.0,
                                   float(yarn_s), int(apply_rope), _ptr(workspace), nbytes,
                                   _dtype_code(q),
                                   _stream(q, stream)))
+
+
+def apex_attn_decode_mla(q, k_cache, v_cache, k_new, v_new, o, m, W=0, base=10000.0,
+                         apply_rope=1, workspace=None, stream=None, yarn_s=1.0):
+    """MLA decode: q [B,H_q,1,d_h+d_r], k_cache [B,H_kv,Sk,d_h+d_r] ([content | rope]),
+    v_cache [B,H_kv,Sk,d_h]; d_r = q width - v width. Other arguments as apex_attn_decode."""
+    B, Hq, _, dqk = q.shape
+    Hkv, Sk, d_h = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("apex_attn_decode_mla",
+           lib().apex_attn_decode_mla(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new),
+                                      _ptr(v_new), _ptr(o), B, Sk, Hq, Hkv, d_h, dqk - d_h,
+                                      int(W), int(m), float(base), float(yarn_s),
+                                      int(apply_rope), _ptr(workspace), nbytes, _dtype_code(q),
+                                      _stream(q, stream)))

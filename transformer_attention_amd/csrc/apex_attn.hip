@@ -87,6 +87,48 @@ int launch_rmsnorm(const apex::RmsNormParams& p, int nc, hipStream_t st) {
   return launch_status();
 }
 
+// Split pass + combine of a decode whose arguments have been checked: q and
+// keys DQK wide with RoPE on their last DR dims, values and output DV wide.
+template <int DQK, int DV, int DR>
+int launch_decode(const void* q, void* k_cache, void* v_cache, const void* k_new,
+                  const void* v_new, void* o, int B, int Sk, int H_q, int H_kv, int W, int64_t m,
+                  double base, double yarn_s, int apply_rope, void* workspace, hipStream_t st) {
+  (void)hipGetLastError();
+  const int G = H_q / H_kv;
+  const int n_hb = (G + apex::kDecHeads - 1) / apex::kDecHeads;
+  const int n_split = decode_splits(B, H_kv, n_hb, Sk);
+  const int n_parts = n_split * apex::kDecWaves;
+  const long long key_lo = W > 0 ? (m - W + 1 > 0 ? m - W + 1 : 0) : 0;
+  const long long n_keys = m - key_lo + 1;
+  long long kpp = (n_keys + n_parts - 1) / n_parts;
+  kpp = (kpp + apex::kDecBN - 1) / apex::kDecBN * apex::kDecBN;
+
+  apex::DecodeParams p{};
+  p.q = (const uint16_t*)q;
+  p.kc = (uint16_t*)k_cache;
+  p.vc = (uint16_t*)v_cache;
+  p.kn = (const uint16_t*)k_new;
+  p.vn = (const uint16_t*)v_new;
+  p.ws_o = (float*)workspace;
+  p.ws_ml = p.ws_o + (size_t)B * H_q * n_parts * DV;
+  p.Sk = Sk; p.Hq = H_q; p.Hkv = H_kv; p.G = G;
+  p.m = m; p.base = base; p.yarn_s = yarn_s; p.apply_rope = apply_rope;
+  p.n_hb = n_hb; p.n_parts = n_parts;
+  p.key_lo = (int)key_lo;
+  p.keys_per_part = (int)kpp;
+  // scores are q.k over all DQK dims
+  p.sc = (float)(kLog2e * yarn_attn_factor(yarn_s) / sqrt((double)DQK));
+  const dim3 grid(n_split, H_kv * n_hb, B);
+  hipLaunchKernelGGL((apex::decode_split_kernel<DQK, DV, DR>), grid, dim3(apex::kDecThreads), 0,
+                     st, p);
+  const int rc = launch_status();
+  if (rc != APEX_OK) return rc;
+  apex::CombineParams c{p.ws_o, p.ws_ml, (uint16_t*)o, B * H_q, n_parts};
+  hipLaunchKernelGGL(apex::decode_combine_kernel<DV>, dim3((B * H_q + 3) / 4), dim3(256), 0, st,
+                     c);
+  return launch_status();
+}
+
 }  // namespace
 
 extern "C" {
@@ -274,47 +316,32 @@ int apex_attn_decode(const void* q, void* k_cache, void* v_cache, const void* k_
   const size_t need = apex_attn_decode_workspace_bytes(B, H_q, H_kv, Sk, d_h);
   if (!workspace || workspace_bytes < need) return APEX_EWORKSPACE;
   if (B > 65535) return APEX_EUNSUPPORTED;
-  hipStream_t st = (hipStream_t)stream;
-  (void)hipGetLastError();
-
-  const int G = H_q / H_kv;
-  const int n_hb = (G + apex::kDecHeads - 1) / apex::kDecHeads;
-  const int n_split = decode_splits(B, H_kv, n_hb, Sk);
-  const int n_parts = n_split * apex::kDecWaves;
-  const long long key_lo = W > 0 ? (m - W + 1 > 0 ? m - W + 1 : 0) : 0;
-  const long long n_keys = m - key_lo + 1;
-  long long kpp = (n_keys + n_parts - 1) / n_parts;
-  kpp = (kpp + apex::kDecBN - 1) / apex::kDecBN * apex::kDecBN;
-
-  apex::DecodeParams p{};
-  p.q = (const uint16_t*)q;
-  p.kc = (uint16_t*)k_cache;
-  p.vc = (uint16_t*)v_cache;
-  p.kn = (const uint16_t*)k_new;
-  p.vn = (const uint16_t*)v_new;
-  p.ws_o = (float*)workspace;
-  p.ws_ml = p.ws_o + (size_t)B * H_q * n_parts * d_h;
-  p.Sk = Sk; p.Hq = H_q; p.Hkv = H_kv; p.G = G;
-  p.m = m; p.base = base; p.yarn_s = yarn_s; p.apply_rope = apply_rope;
-  p.n_hb = n_hb; p.n_parts = n_parts;
-  p.key_lo = (int)key_lo;
-  p.keys_per_part = (int)kpp;
-  p.sc = (float)(kLog2e * yarn_attn_factor(yarn_s) / sqrt((double)d_h));
-  const dim3 grid(n_split, H_kv * n_hb, B);
   if (d_h == 128)
-    hipLaunchKernelGGL(apex::decode_split_kernel<128>, grid, dim3(apex::kDecThreads), 0, st, p);
-  else
-    hipLaunchKernelGGL(apex::decode_split_kernel<64>, grid, dim3(apex::kDecThreads), 0, st, p);
-  int rc = launch_status();
-  if (rc != APEX_OK) return rc;
+    return launch_decode<128, 128, 128>(q, k_cache, v_cache, k_new, v_new, o, B, Sk, H_q, H_kv,
+                                        W, m, base, yarn_s, apply_rope, workspace,
+                                        (hipStream_t)stream);
+  return launch_decode<64, 64, 64>(q, k_cache, v_cache, k_new, v_new, o, B, Sk, H_q, H_kv, W, m,
+                                   base, yarn_s, apply_rope, workspace, (hipStream_t)stream);
+}
 
-  apex::CombineParams c{p.ws_o, p.ws_ml, (uint16_t*)o, B * H_q, n_parts};
-  const dim3 cgrid((B * H_q + 3) / 4);
-  if (d_h == 128)
-    hipLaunchKernelGGL(apex::decode_combine_kernel<128>, cgrid, dim3(256), 0, st, c);
-  else
-    hipLaunchKernelGGL(apex::decode_combine_kernel<64>, cgrid, dim3(256), 0, st, c);
-  return launch_status();
+int apex_attn_decode_mla(const void* q, void* k_cache, void* v_cache, const void* k_new,
+                         const void* v_new, void* o, int B, int Sk, int H_q, int H_kv, int d_h,
+                         int d_r, int W, int64_t m, double base, double yarn_s, int apply_rope,
+                         void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !o || ((k_new == nullptr) != (v_new == nullptr)))
+    return APEX_EINVAL;
+  if (B < 1 || Sk < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || W < 0) return APEX_EINVAL;
+  if (d_h < 2 || (d_h & 1) || d_r < 2 || (d_r & 1)) return APEX_EINVAL;
+  if (m < 0 || m >= Sk || (apply_rope != 0 && apply_rope != 1) || (apply_rope && !(base > 0.0)) ||
+      !yarn_ok(yarn_s))
+    return APEX_EINVAL;
+  if (dtype != APEX_F32 && dtype != APEX_BF16) return APEX_EINVAL;
+  if (dtype != APEX_BF16 || d_h != 128 || d_r != 64) return APEX_EUNSUPPORTED;
+  const size_t need = apex_attn_decode_workspace_bytes(B, H_q, H_kv, Sk, d_h);
+  if (!workspace || workspace_bytes < need) return APEX_EWORKSPACE;
+  if (B > 65535) return APEX_EUNSUPPORTED;
+  return launch_decode<192, 128, 64>(q, k_cache, v_cache, k_new, v_new, o, B, Sk, H_q, H_kv, W,
+                                     m, base, yarn_s, apply_rope, workspace, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -21,6 +21,12 @@
 // When the new token's key/value are given, the wave whose part holds slot m
 // uses them from registers for slot m (so no wave reads slot m from memory in
 // this call) and writes them into the cache.
+//
+// DQK is the width of q and of the cached keys, DV that of the cached values
+// and the output, and RoPE turns the last DR dims of q and of the new key:
+// DQK = DV = DR = d_h for the standard layers, [content d_h | rope d_r] keys
+// (DQK = d_h + d_r, DV = d_h, DR = d_r) for MLA with decoupled RoPE (Part 2,
+// §9.3).
 #pragma once
 #include "device_common.hpp"
 
@@ -33,12 +39,12 @@ constexpr int kDecVPad = 16;  // bf16 pad per LDS V row
 constexpr int kDecHeads = 16; // query heads per wave (MFMA N)
 
 struct DecodeParams {
-  const uint16_t* q;   // [B, Hq, 1, D]
-  uint16_t* kc;        // [B, Hkv, Sk, D]
-  uint16_t* vc;
-  const uint16_t* kn;  // [B, Hkv, 1, D] or null
-  const uint16_t* vn;
-  float* ws_o;         // [B*Hq, n_parts, D]
+  const uint16_t* q;   // [B, Hq, 1, DQK]
+  uint16_t* kc;        // [B, Hkv, Sk, DQK]
+  uint16_t* vc;        // [B, Hkv, Sk, DV]
+  const uint16_t* kn;  // [B, Hkv, 1, DQK] or null
+  const uint16_t* vn;  // [B, Hkv, 1, DV] or null
+  float* ws_o;         // [B*Hq, n_parts, DV]
   float* ws_ml;        // [B*Hq, n_parts, 2]
   int Sk, Hq, Hkv, G;
   long long m;
@@ -49,15 +55,18 @@ struct DecodeParams {
   int n_parts;         // parts per (b, KV head, head block) = gridDim.x * kDecWaves
   int key_lo;          // first visible slot
   int keys_per_part;   // multiple of kDecBN
-  float sc;            // log2(e) / sqrt(D)
+  float sc;            // log2(e) / sqrt(DQK), times the YaRN temperature
 };
 
-template <int D>
+template <int DQK, int DV, int DR>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams p) {
-  constexpr int KK = D / 32;            // 16x16x32 steps over the head dimension
-  constexpr int DB = D / 16;            // 16-row blocks of O^T
-  constexpr int VS = D + kDecVPad;
-  constexpr int VCH = kDecBN * D / 8 / 64;  // 16-byte V chunks per lane per tile
+  static_assert(DQK % 32 == 0 && DV % 16 == 0 && (DQK - DR) % 32 == 0 && DV <= DQK, "widths");
+  constexpr int KK = DQK / 32;          // 16x16x32 steps over the q.k width
+  constexpr int KR = (DQK - DR) / 32;   // first step of the RoPE part
+  constexpr int DB = DV / 16;           // 16-row blocks of O^T
+  constexpr int VS = DV + kDecVPad;
+  constexpr int VCH = kDecBN * DV / 8 / 64;  // 16-byte V chunks per lane per tile
+  constexpr int VCPR = DV / 8;               // 16-byte chunks per V row
   __shared__ __attribute__((aligned(16))) uint16_t vlds[kDecWaves][kDecBN * VS];
 
   const int lane = threadIdx.x & 63;
@@ -75,9 +84,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
 
   const int part_lo = p.key_lo + part * p.keys_per_part;
   const int part_hi = (int)min((long long)part_lo + p.keys_per_part - 1, m);
-  const size_t kv_off = ((size_t)b * p.Hkv + kvh) * p.Sk * D;
-  uint16_t* kcb = p.kc + kv_off;
-  uint16_t* vcb = p.vc + kv_off;
+  const size_t kv_row0 = ((size_t)b * p.Hkv + kvh) * p.Sk;
+  uint16_t* kcb = p.kc + kv_row0 * DQK;
+  uint16_t* vcb = p.vc + kv_row0 * DV;
 
   // ---- Q^T operand: head l16, dims 32kk + 8g4 .. +7, rotated at m ----
   u32x4 qf[KK];
@@ -85,12 +94,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
   for (int kk = 0; kk < KK; kk++) {
     const int d0 = 32 * kk + 8 * g4;
     u32x4 w = u32x4{0, 0, 0, 0};
-    if (head_ok) w = *(const u32x4*)(p.q + ((size_t)b * p.Hq + head) * D + d0);
-    if (p.apply_rope) {
+    if (head_ok) w = *(const u32x4*)(p.q + ((size_t)b * p.Hq + head) * DQK + d0);
+    if (kk >= KR && p.apply_rope) {
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         float c, s;
-        rope_cs_accurate(m, rope_turns(d0 / 2 + e, D, p.base, p.yarn_s), c, s);
+        rope_cs_accurate(m, rope_turns((d0 - (DQK - DR)) / 2 + e, DR, p.base, p.yarn_s), c, s);
         const float x0 = bf16_lo(w[e]), x1 = bf16_hi(w[e]);
         w[e] = pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
       }
@@ -102,23 +111,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
   const bool has_new = p.kn != nullptr && part_lo <= m && m <= part_hi;
   u32x4 knew[KK];
   if (has_new) {
-    const size_t nrow = ((size_t)b * p.Hkv + kvh) * D;
+    const size_t nrow = (size_t)b * p.Hkv + kvh;
 #pragma unroll
     for (int kk = 0; kk < KK; kk++) {
       const int d0 = 32 * kk + 8 * g4;
-      u32x4 w = *(const u32x4*)(p.kn + nrow + d0);
-      if (p.apply_rope) {
+      u32x4 w = *(const u32x4*)(p.kn + nrow * DQK + d0);
+      if (kk >= KR && p.apply_rope) {
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           float c, s;
-          rope_cs_accurate(m, rope_turns(d0 / 2 + e, D, p.base, p.yarn_s), c, s);
+          rope_cs_accurate(m, rope_turns((d0 - (DQK - DR)) / 2 + e, DR, p.base, p.yarn_s), c,
+                           s);
           const float x0 = bf16_lo(w[e]), x1 = bf16_hi(w[e]);
           w[e] = pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
         }
       }
       knew[kk] = w;
-      if (l16 == 0) *(u32x4*)(kcb + (size_t)m * D + d0) = w;  // store into slot m
-      if (l16 == 1) *(u32x4*)(vcb + (size_t)m * D + d0) = *(const u32x4*)(p.vn + nrow + d0);
+      if (l16 == 0) *(u32x4*)(kcb + (size_t)m * DQK + d0) = w;  // store into slot m
+      if (l16 == 1 && d0 < DV)
+        *(u32x4*)(vcb + (size_t)m * DV + d0) = *(const u32x4*)(p.vn + nrow * DV + d0);
     }
   }
 
@@ -129,15 +140,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
       const int key = base + kb * 16 + l16;
 #pragma unroll
       for (int kk = 0; kk < KK; kk++)
-        kreg[kb][kk] = key <= part_hi ? *(const u32x4*)(kcb + (size_t)key * D + 32 * kk + 8 * g4)
-                                      : u32x4{0, 0, 0, 0};
+        kreg[kb][kk] = key <= part_hi
+                           ? *(const u32x4*)(kcb + (size_t)key * DQK + 32 * kk + 8 * g4)
+                           : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int c = 0; c < VCH; c++) {
       const int ci = lane + 64 * c;
-      const int key = base + ci / (D / 8);
-      const int col = (ci % (D / 8)) * 8;
-      vreg[c] = key <= part_hi ? *(const u32x4*)(vcb + (size_t)key * D + col) : u32x4{0, 0, 0, 0};
+      const int key = base + ci / VCPR;
+      const int col = (ci % VCPR) * 8;
+      vreg[c] = key <= part_hi ? *(const u32x4*)(vcb + (size_t)key * DV + col) : u32x4{0, 0, 0, 0};
     }
   };
 
@@ -170,8 +182,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
 #pragma unroll
       for (int c = 0; c < VCH; c++) {
         const int ci = lane + 64 * c;
-        if (ci / (D / 8) == km)
-          vcur[c] = *(const u32x4*)(p.vn + ((size_t)b * p.Hkv + kvh) * D + (ci % (D / 8)) * 8);
+        if (ci / VCPR == km)
+          vcur[c] = *(const u32x4*)(p.vn + ((size_t)b * p.Hkv + kvh) * DV + (ci % VCPR) * 8);
       }
     }
 
@@ -180,7 +192,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
 #pragma unroll
     for (int c = 0; c < VCH; c++) {
       const int ci = lane + 64 * c;
-      *(u32x4*)(vw + (ci / (D / 8)) * VS + (ci % (D / 8)) * 8) = vcur[c];
+      *(u32x4*)(vw + (ci / VCPR) * VS + (ci % VCPR) * 8) = vcur[c];
     }
 
     // S^T = K Q^T: key 16kb + 4g4 + r, head l16
@@ -245,7 +257,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
     const size_t rec = ((size_t)b * p.Hq + head) * p.n_parts + part;
 #pragma unroll
     for (int db = 0; db < DB; db++)
-      *(f32x4*)(p.ws_o + rec * D + 16 * db + 4 * g4) = oacc[db];
+      *(f32x4*)(p.ws_o + rec * DV + 16 * db + 4 * g4) = oacc[db];
     if (g4 == 0) {
       p.ws_ml[rec * 2 + 0] = m_run;
       p.ws_ml[rec * 2 + 1] = l_tot;
