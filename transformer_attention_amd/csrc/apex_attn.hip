@@ -40,7 +40,8 @@ int launch_status() {
 // the standard layers).
 int launch_rope(const void* src, void* dst, long long n_bh, int S, int d_h, int row_len,
                 int64_t m0, double base, double yarn_s, int dtype, hipStream_t st) {
-  apex::RopeParams p{src, dst, n_bh, S, d_h, row_len, (long long)m0, base, yarn_s};
+  apex::RopeParams p{src, dst, n_bh, S, d_h, row_len, (long long)m0,
+                     apex::make_rope_turns(d_h, base, yarn_s)};
   const long long work = n_bh * ((S + apex::kRopeRows - 1) / apex::kRopeRows) * (row_len / 8);
   long long blocks = (work + apex::kRopeThreads - 1) / apex::kRopeThreads;
   if (blocks > 65535LL * 16) blocks = 65535LL * 16;
@@ -112,7 +113,8 @@ int launch_decode(const void* q, void* k_cache, void* v_cache, const void* k_new
   p.ws_o = (float*)workspace;
   p.ws_ml = p.ws_o + (size_t)B * H_q * n_parts * DV;
   p.Sk = Sk; p.Hq = H_q; p.Hkv = H_kv; p.G = G;
-  p.m = m; p.base = base; p.yarn_s = yarn_s; p.apply_rope = apply_rope;
+  p.m = m; p.apply_rope = apply_rope;
+  if (apply_rope) p.turns = apex::make_rope_turns(DR, base, yarn_s);
   p.n_hb = n_hb; p.n_parts = n_parts;
   p.key_lo = (int)key_lo;
   p.keys_per_part = (int)kpp;
@@ -195,7 +197,8 @@ int apex_attn_prefill(const void* q, const void* k, const void* v, void* o, void
     p.o = (uint16_t*)o;
     p.S = S; p.Hq = H_q; p.Hkv = H_kv; p.G = G;
     p.causal = causal; p.W = W; p.P = prefix < S ? prefix : S;
-    p.m0 = m0; p.base = base; p.yarn_s = yarn_s; p.apply_rope = apply_rope != 0;
+    p.m0 = m0; p.apply_rope = apply_rope != 0;
+    if (apply_rope) p.turns = apex::make_rope_turns(d_h, base, yarn_s);
     p.g_pack = head_pack(G);
     p.bm = apex::kPfRows / p.g_pack;
     p.n_pos_tiles = (S + p.bm - 1) / p.bm;
@@ -218,7 +221,8 @@ int apex_attn_prefill(const void* q, const void* k, const void* v, void* o, void
     p.o = (float*)o;
     p.S = S; p.Hq = H_q; p.Hkv = H_kv; p.G = G;
     p.causal = causal; p.W = W; p.P = prefix < S ? prefix : S;
-    p.m0 = m0; p.base = base; p.yarn_s = yarn_s; p.apply_rope = apply_rope != 0;
+    p.m0 = m0; p.apply_rope = apply_rope != 0;
+    if (apply_rope) p.turns = apex::make_rope_turns(d_h, base, yarn_s);
     p.scale = (float)(yarn_attn_factor(yarn_s) / sqrt((double)d_h));
     if (B > 65535 || H_q > 65535) return APEX_EUNSUPPORTED;
     const dim3 grid((S + apex::kF32Rows - 1) / apex::kF32Rows, H_q, B);
@@ -263,7 +267,8 @@ int apex_attn_prefill_mla(const void* q, const void* k, const void* v, void* o,
   p.o = (uint16_t*)o;
   p.S = S; p.Hq = H_q; p.Hkv = H_kv; p.G = G;
   p.causal = causal; p.W = W; p.P = prefix < S ? prefix : S;
-  p.m0 = m0; p.base = base; p.yarn_s = yarn_s; p.apply_rope = apply_rope != 0;
+  p.m0 = m0; p.apply_rope = apply_rope != 0;
+  if (apply_rope) p.turns = apex::make_rope_turns(d_r, base, yarn_s);
   p.g_pack = head_pack(G);
   p.bm = apex::kPfRows / p.g_pack;
   p.n_pos_tiles = (S + p.bm - 1) / p.bm;

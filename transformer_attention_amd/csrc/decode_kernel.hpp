@@ -48,8 +48,7 @@ struct DecodeParams {
   float* ws_ml;        // [B*Hq, n_parts, 2]
   int Sk, Hq, Hkv, G;
   long long m;
-  double base;
-  double yarn_s;      // YaRN scale factor (1 = plain RoPE)
+  RopeTurns turns;     // theta_i / (2 pi) of the DR / 2 rotated pairs (YaRN applied)
   int apply_rope;
   int n_hb;            // ceil(G / 16)
   int n_parts;         // parts per (b, KV head, head block) = gridDim.x * kDecWaves
@@ -99,7 +98,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         float c, s;
-        rope_cs_accurate(m, rope_turns((d0 - (DQK - DR)) / 2 + e, DR, p.base, p.yarn_s), c, s);
+        rope_cs_accurate(m, p.turns.v[(d0 - (DQK - DR)) / 2 + e], c, s);
         const float x0 = bf16_lo(w[e]), x1 = bf16_hi(w[e]);
         w[e] = pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
       }
@@ -120,8 +119,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           float c, s;
-          rope_cs_accurate(m, rope_turns((d0 - (DQK - DR)) / 2 + e, DR, p.base, p.yarn_s), c,
-                           s);
+          rope_cs_accurate(m, p.turns.v[(d0 - (DQK - DR)) / 2 + e], c, s);
           const float x0 = bf16_lo(w[e]), x1 = bf16_hi(w[e]);
           w[e] = pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
         }

@@ -83,10 +83,15 @@ __device__ __forceinline__ buffer_rsrc make_buffer_rsrc(const void* base, uint32
 __device__ __forceinline__ void buffer_to_lds16(buffer_rsrc r, uint32_t voffset, APEX_LDS void* lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, voffset, 0, 0, 0);
 }
+// 16 bytes into registers through a buffer resource (zeros past its size).
+__device__ __forceinline__ u32x4 buffer_load16(buffer_rsrc r, uint32_t voffset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0));
+}
 #else
 struct buffer_rsrc {};
 __device__ __forceinline__ buffer_rsrc make_buffer_rsrc(const void*, uint32_t) { return {}; }
 __device__ __forceinline__ void buffer_to_lds16(buffer_rsrc, uint32_t, APEX_LDS void*) {}
+__device__ __forceinline__ u32x4 buffer_load16(buffer_rsrc, uint32_t) { return u32x4{}; }
 #endif
 
 // ---- RoPE angles -------------------------------------------------------------
@@ -94,7 +99,7 @@ __device__ __forceinline__ void buffer_to_lds16(buffer_rsrc, uint32_t, APEX_LDS 
 // beta_slow = 1: by the wavelength 2 pi / theta, a frequency below 32 stays,
 // one above s is divided by s, and one in between is divided by t s + 1 - t
 // with t = (wavelength - 1) / (s - 1) held to [0, 1]. s = 1: unchanged.
-__device__ __forceinline__ double yarn_theta(double theta, double s) {
+__host__ __device__ inline double yarn_theta(double theta, double s) {
   if (s == 1.0) return theta;
   const double wavelength = 1.0 / (theta * kInvTwoPi);
   if (wavelength < 32.0) return theta;
@@ -103,8 +108,19 @@ __device__ __forceinline__ double yarn_theta(double theta, double s) {
   return theta / (t * s + (1.0 - t));
 }
 // turns_i = theta_i / (2 pi) with theta_i = b^(-2i/d_h) after YaRN (fp64).
-__device__ __forceinline__ double rope_turns(int i, int d_h, double base, double yarn_s) {
+__host__ __device__ inline double rope_turns(int i, int d_h, double base, double yarn_s) {
   return yarn_theta(pow(base, -2.0 * (double)i / (double)d_h), yarn_s) * kInvTwoPi;
+}
+// The turns of every pair of a rotated head of up to 128 dims, formed once on
+// the host per call and passed by value with the kernel arguments.
+constexpr int kMaxRopePairs = 64;
+struct RopeTurns {
+  double v[kMaxRopePairs];
+};
+inline RopeTurns make_rope_turns(int d_rot, double base, double yarn_s) {
+  RopeTurns t{};
+  for (int i = 0; i < d_rot / 2 && i < kMaxRopePairs; i++) t.v[i] = rope_turns(i, d_rot, base, yarn_s);
+  return t;
 }
 // The angle pos * theta_i is formed in fp64 as turns and reduced to [-1/2, 1/2]
 // before any fp32 step, so large positions lose no accuracy.

@@ -27,10 +27,9 @@ struct PrefillF32Params {
   int causal, W;
   int P;              // prefix rows (bidirectional within [0, P)); <= S
   long long m0;
-  double base;
-  double yarn_s;      // YaRN scale factor (1 = plain RoPE)
+  RopeTurns turns;    // theta_i / (2 pi) per pair (YaRN applied)
   int apply_rope;
-  float scale;  // 1 / sqrt(d_h)
+  float scale;  // 1 / sqrt(d_h), times the YaRN temperature
 };
 
 template <int D>
@@ -48,7 +47,7 @@ __global__ __launch_bounds__(kF32Threads) void prefill_f32_kernel(PrefillF32Para
   const int kvh = h / p.G;
 
   if (p.apply_rope) {
-    if (tid < D / 2) turns_lds[tid] = rope_turns(tid, D, p.base, p.yarn_s);
+    if (tid < D / 2) turns_lds[tid] = p.turns.v[tid];
     __syncthreads();
   }
 

@@ -61,8 +61,7 @@ struct PrefillParams {
   int causal, W;
   int P;              // prefix rows (bidirectional within [0, P)); <= S
   long long m0;
-  double base;
-  double yarn_s;      // YaRN scale factor (1 = plain RoPE)
+  RopeTurns turns;    // theta_i / (2 pi) of the rotated pairs (YaRN applied)
   int apply_rope;     // rotate q while it loads
   int g_pack;         // query heads per workgroup (divides G, <= kPfWaves)
   int bm;             // positions per workgroup = kPfRows / g_pack
@@ -117,11 +116,16 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
   static_assert(LOADSK * kPfWaves * 1024 == TILEK && LOADSV * kPfWaves * 1024 == TILEV,
                 "tile split");
 
+  constexpr int NP = DR / 2;  // rotated pairs per row
+  constexpr int CH = NP / 2;  // 16-byte chunks (two (cos, sin) pairs) per table row
+  static_assert(CH == 16 || CH == 32, "angle table swizzle");
+  static_assert(32 * NP * 8 <= TILEV, "angle table fits one V slot");
+
   __shared__ __attribute__((aligned(1024))) unsigned char kbuf[2][TILEK];
   __shared__ __attribute__((aligned(1024))) unsigned char vbuf[2][TILEV];
-  // The RoPE turns are needed only while Q loads, before V slot 1 first
-  // receives a tile (after the prologue's second barrier): they borrow it.
-  double* const turns_lds = (double*)vbuf[1];
+  // The Q angle table is needed only while Q loads, before V slot 1 first
+  // receives a tile (after the prologue's second barrier): it borrows it.
+  float2* const cs_lds = (float2*)vbuf[1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -178,42 +182,85 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
         make_buffer_rsrc(kg + (size_t)t * kPfBN * DQK, (uint32_t)(p.S - t * kPfBN) * RBK);
 #pragma unroll
     for (int i = 0; i < LOADSK; i++)
-      buffer_to_lds16(r, ldk_off[i], (APEX_LDS void*)(dst + (wave + i * kPfWaves) * 1024));
+      buffer_to_lds16(r, ldk_off[i],
+                      (APEX_LDS void*)(uintptr_t)(lds_addr(dst) + (wave + i * kPfWaves) * 1024));
   };
   auto issue_v = [&](unsigned char* dst, int t) {
     const buffer_rsrc r =
         make_buffer_rsrc(vg + (size_t)t * kPfBN * DV, (uint32_t)(p.S - t * kPfBN) * RBV);
 #pragma unroll
     for (int i = 0; i < LOADSV; i++)
-      buffer_to_lds16(r, ldv_off[i], (APEX_LDS void*)(dst + (wave + i * kPfWaves) * 1024));
+      buffer_to_lds16(r, ldv_off[i],
+                      (APEX_LDS void*)(uintptr_t)(lds_addr(dst) + (wave + i * kPfWaves) * 1024));
   };
+
+  // When all waves hold the same 32 positions (a pack of 4 heads), cos/sin of
+  // (m0 + p0 + r) theta_i are formed once per workgroup into an LDS table
+  // [32 rows][NP pairs] and shared by the heads; 16-byte chunks are XORed
+  // with the row so the 16 rows one read cycle serves hit distinct banks.
+  // Thread tid fills the entries of pair tid % NP (kPfThreads is a multiple
+  // of NP), so it needs one frequency, fetched before the big loads.
+  static_assert(kPfThreads % NP == 0, "one frequency per thread");
+  const bool shared_cs = p.apply_rope && pos_blocks == 1;
+  const double my_turns = shared_cs ? p.turns.v[tid % NP] : 0.0;
+
+  // ---- Q^T operand: lane holds row `row`, dims 16kk + 8g .. +7 ----
+  // Its loads go out first so their latency overlaps the first tiles'; the
+  // buffer covers this head's S rows, so rows past S read as zeros.
+  u32x4 qf[KK];
+  {
+    const buffer_rsrc qr =
+        make_buffer_rsrc(p.q + ((size_t)b * p.Hq + head) * p.S * DQK, (uint32_t)p.S * RBK);
+    const uint32_t qoff = (uint32_t)row * RBK + 16 * g;
+#pragma unroll
+    for (int kk = 0; kk < KK; kk++) qf[kk] = buffer_load16(qr, qoff + 32 * kk);
+  }
 
   issue_k(kbuf[0], t_lo);
   issue_v(vbuf[0], t_lo);
   if (t_lo < t_hi) issue_k(kbuf[1], t_lo + 1);
 
-  if (p.apply_rope && tid < DR / 2) turns_lds[tid] = rope_turns(tid, DR, p.base, p.yarn_s);
+  // The angles are formed while the loads are in flight and written to LDS
+  // after them (the table shares LDS with the tiles' direct loads).
+  constexpr int NE = 32 * NP / kPfThreads;  // table entries per thread
+  const int pr = tid % NP;
+  float tc[NE], ts[NE];
+  if (shared_cs) {
+#pragma unroll
+    for (int i = 0; i < NE; i++)
+      rope_cs_fast(p.m0 + p0 + tid / NP + i * (kPfThreads / NP), my_turns, tc[i], ts[i]);
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's tile loads have landed
-  __syncthreads();                                    // ... and every other wave's
+  if (shared_cs) {
+#pragma unroll
+    for (int i = 0; i < NE; i++) {
+      const int r = tid / NP + i * (kPfThreads / NP);
+      cs_lds[(r * CH + ((pr >> 1) ^ (r & (CH - 1)))) * 2 + (pr & 1)] = float2{tc[i], ts[i]};
+    }
+  }
+  __syncthreads();  // every wave's tile loads and table entries are in LDS
 
-  // ---- Q^T operand: lane holds row `row`, dims 16kk + 8g .. +7 ----
-  u32x4 qf[KK];
-  {
-    const uint16_t* qrow = p.q + (((size_t)b * p.Hq + head) * p.S + row) * DQK;
+  // ---- RoPE of the Q operand ----
+  if (p.apply_rope) {
 #pragma unroll
-    for (int kk = 0; kk < KK; kk++) {
-      const int d0 = 16 * kk + 8 * g;
-      u32x4 w = row < p.S ? *(const u32x4*)(qrow + d0) : u32x4{0, 0, 0, 0};
-      if (kk >= KR && p.apply_rope) {  // the RoPE part: pairs of a DR-wide head
+    for (int kk = KR; kk < KK; kk++) {  // the RoPE part: pairs of a DR-wide head
+      const int pr0 = (16 * kk + 8 * g - (DQK - DR)) / 2;  // first of this lane's 4 pairs
+      float c[4], s[4];
+      if (shared_cs) {
+        const int sw = r32 & (CH - 1);
+        const f32x4 a = *(const f32x4*)&cs_lds[(r32 * CH + ((pr0 >> 1) ^ sw)) * 2];
+        const f32x4 z = *(const f32x4*)&cs_lds[(r32 * CH + (((pr0 >> 1) + 1) ^ sw)) * 2];
+        c[0] = a[0]; s[0] = a[1]; c[1] = a[2]; s[1] = a[3];
+        c[2] = z[0]; s[2] = z[1]; c[3] = z[2]; s[3] = z[3];
+      } else {
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          float c, s;
-          rope_cs_fast(p.m0 + row, turns_lds[(d0 - (DQK - DR)) / 2 + e], c, s);
-          const float x0 = bf16_lo(w[e]), x1 = bf16_hi(w[e]);
-          w[e] = pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
-        }
+        for (int e = 0; e < 4; e++) rope_cs_fast(p.m0 + row, p.turns.v[pr0 + e], c[e], s[e]);
       }
-      qf[kk] = w;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const float x0 = bf16_lo(qf[kk][e]), x1 = bf16_hi(qf[kk][e]);
+        qf[kk][e] = pack_bf16x2(x0 * c[e] - x1 * s[e], x0 * s[e] + x1 * c[e]);
+      }
     }
   }
 

@@ -31,8 +31,7 @@ struct RopeParams {
   int d_h;             // width of the rotated part (its frequencies follow d_h)
   int row_len;         // elements per row, >= d_h; the rotated part is the last d_h
   long long m0;
-  double base;
-  double yarn_s;      // YaRN scale factor (1 = plain RoPE)
+  RopeTurns turns;     // theta_i / (2 pi) of the d_h / 2 pairs (YaRN applied)
 };
 
 template <typename T>
@@ -70,10 +69,10 @@ struct RopeIO<float> {  // fp32: 8 elements = 32 bytes
 
 template <typename T>
 __global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeParams p) {
-  __shared__ double turns_lds[128];  // theta_i / (2 pi), i < d_h / 2 <= 128
-  __shared__ float step_c[128], step_s[128];  // cos, sin of theta_i (one position)
+  __shared__ double turns_lds[kMaxRopePairs];  // theta_i / (2 pi), i < d_h / 2
+  __shared__ float step_c[kMaxRopePairs], step_s[kMaxRopePairs];  // cos, sin of theta_i
   if ((int)threadIdx.x < p.d_h / 2) {
-    const double turns = rope_turns(threadIdx.x, p.d_h, p.base, p.yarn_s);
+    const double turns = p.turns.v[threadIdx.x];
     turns_lds[threadIdx.x] = turns;
     rope_cs_accurate(1, turns, step_c[threadIdx.x], step_s[threadIdx.x]);
   }
