@@ -370,6 +370,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
       for (int db = 0; db < DB; db++) oacc[db] *= alpha;
     }
 
+    // The two workgroups' waves share each SIMD; while this wave accumulates
+    // P V it yields issue priority to a wave in its score/softmax phase, whose
+    // vector work can then run beside these matrix-core instructions.
+    __builtin_amdgcn_s_setprio(0);
     // O^T += V^T P^T. Operand k-index 8g+e <-> key kb*32 + 16c + 4g + e (e < 4)
     // and kb*32 + 16c + 8 + 4g + (e - 4) (e >= 4), matching the S^T layout.
     const unsigned char* vb = vbuf[it & 1];
@@ -384,6 +388,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
           const u32x2 hi = lds_read_tr16((const uint16_t*)(vb + koff + v_off[1][db]));
           oacc[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pk[kb][c], oacc[db]);
         }
+    __builtin_amdgcn_s_setprio(1);  // back to the score/softmax phase
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // V(t+1), K(t+2) have landed
     __syncthreads();
   };
