@@ -400,20 +400,33 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
   }
 
   // ---- epilogue: O = O^T / l, rounded to bf16 ----
+  // A lane holds 4-dim pieces of one row, so direct stores would scatter over
+  // 32 rows per instruction. The rows go through this wave's slice of the K
+  // buffers (free after the last barrier) instead: written as held, read back
+  // as whole 16-byte chunks, stored as four complete rows (1 KB contiguous)
+  // per instruction. 16-byte chunks are XORed with the row against bank
+  // conflicts.
+  constexpr int CHV = DV / 8;  // 16-byte chunks per O row
+  static_assert(kPfWaves * 32 * DV * 2 <= 2 * TILEK, "O staging fits the K buffers");
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (row < p.S) {
-    const float inv = 1.0f / l_tot;
-    uint16_t* orow = p.o + (((size_t)b * p.Hq + head) * p.S + row) * DV;
+  const float inv = 1.0f / l_tot;
+  unsigned char* const ost = &kbuf[0][0] + wave * 32 * DV * 2;
 #pragma unroll
-    for (int db = 0; db < DB; db++)
+  for (int db = 0; db < DB; db++)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; q4++) {
-        const int d = db * 32 + 8 * q4 + 4 * g;
-        u32x2 w;
-        w[0] = pack_bf16x2(oacc[db][4 * q4 + 0] * inv, oacc[db][4 * q4 + 1] * inv);
-        w[1] = pack_bf16x2(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv);
-        *(u32x2*)(orow + d) = w;
-      }
+    for (int q4 = 0; q4 < 4; q4++) {
+      const int c = 4 * db + q4;  // chunk of dims 8c .. 8c+7; lane half g holds 4 of them
+      u32x2 w;
+      w[0] = pack_bf16x2(oacc[db][4 * q4 + 0] * inv, oacc[db][4 * q4 + 1] * inv);
+      w[1] = pack_bf16x2(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv);
+      *(u32x2*)(ost + r32 * (DV * 2) + ((c ^ (r32 & (CHV - 1))) << 4) + 8 * g) = w;
+    }
+  uint16_t* const ohead = p.o + ((size_t)b * p.Hq + head) * p.S * DV;
+#pragma unroll
+  for (int i = 0; i < 32 * CHV / 64; i++) {
+    const int rr = i * (64 / CHV) + lane / CHV, c = lane % CHV;
+    const u32x4 v = *(const u32x4*)(ost + rr * (DV * 2) + ((c ^ (rr & (CHV - 1))) << 4));
+    if (pw + rr < p.S) *(u32x4*)(ohead + (size_t)(pw + rr) * DV + 8 * c) = v;
   }
 }
 
