@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
 #pragma unroll
       for (int kk = 0; kk < KK; kk++)
         kreg[kb][kk] = key <= part_hi
-                           ? *(const u32x4*)(kcb + (size_t)key * DQK + 32 * kk + 8 * g4)
+                           ? __builtin_nontemporal_load((const u32x4*)(kcb + (size_t)key * DQK + 32 * kk + 8 * g4))
                            : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
@@ -147,7 +147,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
       const int ci = lane + 64 * c;
       const int key = base + ci / VCPR;
       const int col = (ci % VCPR) * 8;
-      vreg[c] = key <= part_hi ? *(const u32x4*)(vcb + (size_t)key * DV + col) : u32x4{0, 0, 0, 0};
+      vreg[c] = key <= part_hi ? __builtin_nontemporal_load((const u32x4*)(vcb + (size_t)key * DV + col))
+                               : u32x4{0, 0, 0, 0};
     }
   };
 
