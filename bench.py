@@ -112,6 +112,24 @@ def load_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
+SETTLE_S = 0.3  # untimed work before the warm-up steps of each timed workload
+
+
+def settle(torch, fn):
+    """Run fn untimed for about SETTLE_S seconds of wall time, so the GPU's
+    clocks have left their idle state before the warm-up steps; a few
+    milliseconds of work at the start of a run measure ~20% slow otherwise."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(4):
+            fn()
+        n += 4
+        torch.cuda.synchronize()
+    return n
+
+
 def time_prefill(taa, torch, name, steps, warmup):
     import apex_inputs
     w = apex_inputs.WORKLOADS[name]
@@ -139,6 +157,7 @@ def time_prefill(taa, torch, name, steps, warmup):
         if ev:
             ev[2].record()
 
+    settle(torch, step)
     for _ in range(warmup):
         step()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
@@ -160,6 +179,7 @@ def time_rmsnorm(taa, torch, name, steps, warmup):
     w = apex_inputs.WORKLOADS[name]
     x, g = apex_inputs.workload_inputs(name, device="cuda")
     y = torch.empty_like(x)
+    settle(torch, lambda: taa.apex_rmsnorm(x, g, y, eps=w["eps"]))
     for _ in range(warmup):
         taa.apex_rmsnorm(x, g, y, eps=w["eps"])
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -189,6 +209,7 @@ def time_decode(taa, torch, steps, warmup, name=DECODE):
     def call():
         fn(q, kc, vc, kn, vn, o, m=w["m"], W=w["W"], base=w["base"], workspace=ws)
 
+    settle(torch, call)
     for _ in range(warmup):
         call()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -287,8 +308,8 @@ def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--headline-only", action="store_true",
@@ -328,7 +349,7 @@ def main():
 
     extra = {}
     if not args.headline_only:
-        dsteps = max(5, args.steps)
+        dsteps = max(5, args.steps // 10)
         log("timing %s: %d warmup + %d calls" % (DECODE, args.warmup, dsteps))
         dw, d_mean, d_med, d_min = time_decode(taa, torch, dsteps, args.warmup)
         dbytes = decode_bytes(dw)
@@ -355,8 +376,8 @@ def main():
         others = {}
         for name in OTHERS:
             log("timing %s" % name)
-            ow, oms, orope, oattn, _ = time_prefill(taa, torch, name, max(3, args.steps // 4),
-                                                    2)
+            ow, oms, orope, oattn, _ = time_prefill(taa, torch, name, max(3, args.steps // 25),
+                                                    3)
             of = prefill_flops(ow)
             others[name] = {"ms_per_step": round(oms, 4), "rope_k_ms": round(orope, 4),
                             "attention_ms": round(oattn, 4),
@@ -372,7 +393,7 @@ def main():
         norms = {}
         for name in RMSNORMS:
             log("timing %s" % name)
-            rw, rms_mean, rms_min = time_rmsnorm(taa, torch, name, max(10, args.steps), 3)
+            rw, rms_mean, rms_min = time_rmsnorm(taa, torch, name, max(10, args.steps // 5), 3)
             rb = rmsnorm_bytes(rw)
             norms[name] = {"ms_per_call": round(rms_mean, 4), "ms_min": round(rms_min, 4),
                            "algorithmic_bytes": rb,
@@ -389,6 +410,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": SETTLE_S,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

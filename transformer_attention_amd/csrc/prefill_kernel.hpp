@@ -33,11 +33,16 @@
 //   both the K reads (16 rows, same chunk) and the transposed V reads (4 rows
 //   x 4 chunks per half wave) hit distinct banks.
 //
-// Online softmax (fp32): scores are scaled by log2(e)/sqrt(d_h) so exp2 can
-// be used. The running max m only moves when a tile's max exceeds it by more
-// than 8 (in log2 units): probabilities stay <= 2^8, and O and the running
-// sum l are rescaled by exp2(m_old - m_new) only then. O / l is exact for any
-// such choice of m.
+// Online softmax (fp32, log2 units): Q is multiplied by log2(e)/sqrt(d_h) as
+// it is rotated and rounded to bf16, so a score is already the exponent for
+// exp2. Each S^T chain starts its accumulator at -m (the running max as it
+// was when the chain was issued) instead of zero, so the matrix cores deliver
+// s - m and a probability costs one exp2, with no per-score vector arithmetic.
+// The running max only moves when a tile's max exceeds it by more than 8:
+// probabilities stay <= 2^8, and O and the running sum l are rescaled by
+// exp2(m_old - m_new) only then; a tile whose chain started from an older m
+// has its exponentials recomputed with the difference (rare: the first tiles
+// of a row). O / l is exact for any such choice of m.
 #pragma once
 #include "device_common.hpp"
 
@@ -129,7 +134,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar
   const int r32 = lane & 31;
   const int g = lane >> 5;
 
@@ -227,8 +232,11 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
   float tc[NE], ts[NE];
   if (shared_cs) {
 #pragma unroll
-    for (int i = 0; i < NE; i++)
+    for (int i = 0; i < NE; i++) {  // entries carry the score scale
       rope_cs_fast(p.m0 + p0 + tid / NP + i * (kPfThreads / NP), my_turns, tc[i], ts[i]);
+      tc[i] *= p.sc;
+      ts[i] *= p.sc;
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's tile loads have landed
   if (shared_cs) {
@@ -240,7 +248,17 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
   }
   __syncthreads();  // every wave's tile loads and table entries are in LDS
 
-  // ---- RoPE of the Q operand ----
+  // ---- RoPE and score scale of the Q operand ----
+  // q' = RoPE(q) * log2(e)/sqrt(d_h), rounded to bf16 once; dims outside the
+  // rotated part (and all of them when nothing is rotated) are only scaled.
+  const int kr_end = p.apply_rope ? KR : KK;
+#pragma unroll
+  for (int kk = 0; kk < KK; kk++)
+    if (kk < kr_end) {
+#pragma unroll
+      for (int e = 0; e < 4; e++)
+        qf[kk][e] = pack_bf16x2(bf16_lo(qf[kk][e]) * p.sc, bf16_hi(qf[kk][e]) * p.sc);
+    }
   if (p.apply_rope) {
 #pragma unroll
     for (int kk = KR; kk < KK; kk++) {  // the RoPE part: pairs of a DR-wide head
@@ -254,7 +272,11 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
         c[2] = z[0]; s[2] = z[1]; c[3] = z[2]; s[3] = z[3];
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; e++) rope_cs_fast(p.m0 + row, p.turns.v[pr0 + e], c[e], s[e]);
+        for (int e = 0; e < 4; e++) {
+          rope_cs_fast(p.m0 + row, p.turns.v[pr0 + e], c[e], s[e]);
+          c[e] *= p.sc;
+          s[e] *= p.sc;
+        }
       }
 #pragma unroll
       for (int e = 0; e < 4; e++) {
@@ -265,10 +287,24 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
   }
 
   // ---- per-lane LDS offsets (loop invariant) ----
-  // K operand: row kb*32 + r32, logical chunk 2kk + g.
-  int k_off[KK];
+  // K operand: row kb*32 + r32, logical chunk 2kk + g. With 24-chunk rows
+  // the offsets are formed in the loop instead of held: the swizzle only
+  // flips bits 5-6 of the byte offset (kk mod 4 selects which), and kk / 4
+  // adds 128 bytes, so offset(kk) = (offset(0) ^ 32 (kk mod 4)) + 128 (kk / 4).
+  constexpr bool kXorK = CPRK == 24;
+  int k_off[kXorK ? 1 : KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; kk++) k_off[kk] = r32 * RBK + (slot<CPRK>(2 * kk + g, r32) << 4);
+  for (int kk = 0; kk < (kXorK ? 1 : KK); kk++)
+    k_off[kk] = r32 * RBK + (slot<CPRK>(2 * kk + g, r32) << 4);
+  const uint32_t kq = lds_addr(kbuf[0]) + (uint32_t)k_off[0];
+  auto k_operand = [&](const unsigned char* kb_lds, int kb, int kk) {
+    if (kXorK) {
+      const uint32_t a = (opaque(kq) ^ (uint32_t)(32 * (kk & 3))) +
+                         (uint32_t)(kb_lds - &kbuf[0][0]) + kb * 32 * RBK + 128 * (kk >> 2);
+      return lds_read16_at(a);
+    }
+    return *(const u32x4*)(kb_lds + kb * 32 * RBK + k_off[kk]);
+  };
   // V^T operand via ds_read_b64_tr_b16: lane j16 of 16-lane group qg reads 8 bytes
   // at row key + j16/4, columns 32db + 16(qg&1) + 4(j16&3): logical chunk
   // 4db + 2(qg&1) + (j16&3)/2, half (j16&1). Rows +8 give the k-indices 4..7.
@@ -285,13 +321,18 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
     }
   }
 
-  auto qk = [&](const unsigned char* kb_lds, f32x16 (&s)[2]) {
+  // S^T - m for 64 keys: both 32-key chains start from -m (every element of
+  // a lane holds its row's value).
+  auto qk = [&](const unsigned char* kb_lds, f32x16 (&s)[2], float m) {
+    f32x16 negm;
+#pragma unroll
+    for (int r = 0; r < 16; r++) negm[r] = -m;
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) {
-      s[kb] = f32x16{};
+      s[kb] = negm;
 #pragma unroll
       for (int kk = 0; kk < KK; kk++)
-        s[kb] = mfma32(*(const u32x4*)(kb_lds + kb * 32 * RBK + k_off[kk]), qf[kk], s[kb]);
+        s[kb] = mfma32(k_operand(kb_lds, kb, kk), qf[kk], s[kb]);
     }
   };
 
@@ -303,50 +344,79 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; db++) oacc[db] = f32x16{};
-  float m_run = kNegInf, l_run = 0.0f;
+  // m_run: running row max (log2 units, -inf until a key is seen); m_use:
+  // its finite stand-in, which O and l are relative to and the next S^T chain
+  // starts from; m_a: the value the chain of s_cur started from.
+  float m_run = kNegInf, m_use = 0.0f, m_a = 0.0f, l_run = 0.0f;
 
-  f32x16 sa[2], sb[2];
-  qk(kbuf[0], sa);
-  bool full_a = tile_is_full(t_lo * kPfBN, pw, p.S, p.causal, p.W, p.P), full_b = true;
-  __syncthreads();  // every wave is done with kbuf[0] before K(t_lo + 2) lands there
-
-  // One 64-key tile: S(t+1) = K(t+1) Q^T is issued to the matrix cores while
-  // the vector ALUs run the softmax of S(t); then O += P(t) V(t).
-  auto step = [&](int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2], bool& full_cur,
-                  bool& full_next) {
-    const int it = t - t_lo;
-    if (t + 1 <= t_hi) issue_v(vbuf[(it + 1) & 1], t + 1);
-    if (t + 2 <= t_hi) issue_k(kbuf[it & 1], t + 2);
-
-    if (!full_cur) {  // per-element mask of tile t
+  // Tile t's mask (unless the tile is full) and the row max of its scores,
+  // absolute (both halves of the wave hold keys of the row).
+  auto mask_max = [&](int t, f32x16 (&sc)[2], bool full, float m_from) {
+    if (!full) {
       const int base = t * kPfBN + 4 * g - vis_lo;
 #pragma unroll
       for (int kb = 0; kb < 2; kb++)
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const unsigned off = (unsigned)(base + kb * 32 + 8 * (r >> 2) + (r & 3));
-          s_cur[kb][r] = off <= vis_span ? s_cur[kb][r] : kNegInf;
+          sc[kb][r] = off <= vis_span ? sc[kb][r] : kNegInf;
         }
     }
-
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) mx = fmaxf(mx, s_cur[kb][r]);
-    mx = wave_max_xor(mx, 32) * p.sc;
-    // the max moves (for every lane of the wave) only when some lane's tile max
-    // exceeds its running max by more than kLazyMax
-    const bool grow = __builtin_amdgcn_ballot_w64(mx > m_run + kLazyMax) != 0;
-    const float m_new = grow ? fmaxf(m_run, mx) : m_run;
-    const float m_use = m_new == kNegInf ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+      for (int r = 0; r < 16; r++) mx = fmaxf(mx, sc[kb][r]);
+    return fmaxf(mx, lane_xor32(mx)) + m_from;
+  };
 
-    // S(t+1): on the last tile this reads a stale buffer and is discarded
-    qk(kbuf[(it + 1) & 1], s_next);
-    full_next = tile_is_full((t + 1) * kPfBN, pw, p.S, p.causal, p.W, p.P);
+  f32x16 sa[2], sb[2];
+  qk(kbuf[0], sa, 0.0f);
+  const bool full_lo = tile_is_full(t_lo * kPfBN, pw, p.S, p.causal, p.W, p.P);
+  float mx_a = mask_max(t_lo, sa, full_lo, 0.0f), mx_b = kNegInf;
+  __syncthreads();  // every wave is done with kbuf[0] before K(t_lo + 2) lands there
 
+  // One 64-key tile. On entry s_cur = S(t) - m_a, masked, with row max mx_cur.
+  // The max update comes first, so S(t+1) - m = K(t+1) Q^T - m is issued to
+  // the matrix cores with the current m while the vector ALUs run the
+  // exponentials of S(t); then O += P(t) V(t), beside which S(t+1) is masked
+  // and its max taken. On the last tile (LAST) nothing further is loaded or
+  // issued and no barrier follows: no wave reads the K buffers after the
+  // previous tile's barrier.
+  auto step = [&](int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2], float mx_cur, float& mx_next,
+                  auto last_c) {
+    constexpr bool LAST = decltype(last_c)::value != 0;
+    const int it = t - t_lo;
+    if (!LAST) {
+      issue_v(vbuf[(it + 1) & 1], t + 1);
+      if (t + 2 <= t_hi) issue_k(kbuf[it & 1], t + 2);
+    }
+
+    // the max moves (for every lane of the wave) only when some lane's tile
+    // max exceeds its running max by more than kLazyMax
+    if (__builtin_amdgcn_ballot_w64(mx_cur > m_run + kLazyMax) != 0) {  // wave-uniform, rare
+      const float m_new = fmaxf(m_run, mx_cur);
+      const float m_new_use = m_new == kNegInf ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new_use);
+      m_run = m_new;
+      m_use = m_new_use;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; db++) oacc[db] *= alpha;
+    }
+    // scores from a chain that started at an older m move to the current one
+    if (__builtin_amdgcn_ballot_w64(m_use != m_a) != 0) {
+      const float shift = m_use - m_a;
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) s_cur[kb][r] -= shift;
+    }
+    m_a = m_use;
+
+    if (!LAST) qk(kbuf[(it + 1) & 1], s_next, m_use);
+
+    // P(t) = exp2(s - m), rounded to bf16 as the P V operand, and its row sum
     float lsum = 0.0f;
     u32x4 pk[2][2];
 #pragma unroll
@@ -355,20 +425,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
       for (int c = 0; c < 2; c++)
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-          const float e0 =
-              __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][8 * c + 2 * e], p.sc, -m_use));
-          const float e1 =
-              __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][8 * c + 2 * e + 1], p.sc, -m_use));
+          const float e0 = __builtin_amdgcn_exp2f(s_cur[kb][8 * c + 2 * e]);
+          const float e1 = __builtin_amdgcn_exp2f(s_cur[kb][8 * c + 2 * e + 1]);
           pk[kb][c][e] = pack_bf16x2(e0, e1);
           lsum = add_bf16x2(pk[kb][c][e], lsum);  // the row sum of the rounded P that P V uses
         }
-    // keep the exponentials next to the S(t+1) MFMAs (not sunk past the branch)
-    asm volatile("" ::"v"(pk[0][0]), "v"(pk[0][1]), "v"(pk[1][0]), "v"(pk[1][1]));
-    l_run = l_run * alpha + lsum;
-    if (grow) {  // wave-uniform, rare after the first tiles
-#pragma unroll
-      for (int db = 0; db < DB; db++) oacc[db] *= alpha;
-    }
+    l_run += lsum;
 
     // The two workgroups' waves share each SIMD; while this wave accumulates
     // P V it yields issue priority to a wave in its score/softmax phase, whose
@@ -388,15 +450,26 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
           const u32x2 hi = lds_read_tr16((const uint16_t*)(vb + koff + v_off[1][db]));
           oacc[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pk[kb][c], oacc[db]);
         }
+    if (!LAST)
+      mx_next = mask_max(t + 1, s_next,
+                         tile_is_full((t + 1) * kPfBN, pw, p.S, p.causal, p.W, p.P), m_use);
     __builtin_amdgcn_s_setprio(1);  // back to the score/softmax phase
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // V(t+1), K(t+2) have landed
-    __syncthreads();
+    if (!LAST) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // V(t+1), K(t+2) have landed
+      __syncthreads();
+    }
   };
 
-  for (int t = t_lo; t <= t_hi; t += 2) {
-    step(t, sa, sb, full_a, full_b);
-    if (t + 1 > t_hi) break;
-    step(t + 1, sb, sa, full_b, full_a);
+  int t = t_lo;
+  for (; t + 2 <= t_hi; t += 2) {
+    step(t, sa, sb, mx_a, mx_b, Int<0>{});
+    step(t + 1, sb, sa, mx_b, mx_a, Int<0>{});
+  }
+  if (t < t_hi) {
+    step(t, sa, sb, mx_a, mx_b, Int<0>{});
+    step(t + 1, sb, sa, mx_b, mx_a, Int<1>{});
+  } else {
+    step(t, sa, sb, mx_a, mx_b, Int<1>{});
   }
 
   // ---- epilogue: O = O^T / l, rounded to bf16 ----
@@ -408,7 +481,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
   // conflicts.
   constexpr int CHV = DV / 8;  // 16-byte chunks per O row
   static_assert(kPfWaves * 32 * DV * 2 <= 2 * TILEK, "O staging fits the K buffers");
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = l_run + lane_xor32(l_run);
   const float inv = 1.0f / l_tot;
   unsigned char* const ost = &kbuf[0][0] + wave * 32 * DV * 2;
 #pragma unroll
