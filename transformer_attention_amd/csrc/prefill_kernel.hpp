@@ -351,7 +351,19 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
 
   // Tile t's mask (unless the tile is full) and the row max of its scores,
   // absolute (both halves of the wave hold keys of the row).
+  // The max is taken first over the unmasked scores, so that it needs no
+  // branch and can run beside the P V matrix instructions; a partial tile
+  // (rare: the diagonal and window edges) is then masked and its max retaken.
+  auto row_max = [&](const f32x16 (&sc)[2]) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) mx = fmaxf(mx, sc[kb][r]);
+    return fmaxf(mx, lane_xor32(mx));
+  };
   auto mask_max = [&](int t, f32x16 (&sc)[2], bool full, float m_from) {
+    float mx = row_max(sc);
     if (!full) {
       const int base = t * kPfBN + 4 * g - vis_lo;
 #pragma unroll
@@ -361,13 +373,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
           const unsigned off = (unsigned)(base + kb * 32 + 8 * (r >> 2) + (r & 3));
           sc[kb][r] = off <= vis_span ? sc[kb][r] : kNegInf;
         }
+      mx = row_max(sc);
     }
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) mx = fmaxf(mx, sc[kb][r]);
-    return fmaxf(mx, lane_xor32(mx)) + m_from;
+    return mx + m_from;
   };
 
   f32x16 sa[2], sb[2];
@@ -430,6 +438,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
           pk[kb][c][e] = pack_bf16x2(e0, e1);
           lsum = add_bf16x2(pk[kb][c][e], lsum);  // the row sum of the rounded P that P V uses
         }
+    // the row sum is formed here, beside the S(t+1) matrix instructions, not
+    // sunk to where l is next needed
+    asm volatile("" ::"v"(lsum));
     l_run += lsum;
 
     // The two workgroups' waves share each SIMD; while this wave accumulates
