@@ -113,6 +113,7 @@ def load_traffic():
 
 
 SETTLE_S = 0.3  # untimed work before the warm-up steps of each timed workload
+EVENT_EVERY = 8  # per-launch events on one step in EVENT_EVERY (see time_prefill)
 
 
 def settle(torch, fn):
@@ -143,18 +144,27 @@ def time_prefill(taa, torch, name, steps, warmup):
         # the MLA call rotates the key rope parts and runs the attention in one call
         o = torch.empty(q.shape[:3] + (w["d"],), dtype=q.dtype, device=q.device)
 
-    def step(ev=None):
-        if ev:
+    # Per-launch HIP events go on a sample of the timed steps only: each
+    # record costs about 3.5 us of GPU time, so recording around both launches
+    # of every step would slow the very steps whose wall time is reported.
+    # Step i records around its RoPE launch when i % every == every // 2,
+    # around its attention launch when i % every == 0 (every step of a short run).
+    every = EVENT_EVERY if steps >= 2 * EVENT_EVERY else 1
+
+    def step(i=-1, ev=None):
+        samp_attn = ev is not None and i % every == 0
+        samp_rope = ev is not None and i % every == every // 2
+        if samp_rope:
             ev[0].record()
         if w["kind"] != "mla_prefill":
             taa.apex_rope_qk(None, k, k_out=kr, m0=w["m0"], base=w["base"], yarn_s=ys)
-        if ev:
+        if samp_rope or samp_attn:
             ev[1].record()
         if w["kind"] == "mla_prefill":
             taa.apex_attn_prefill_mla(q, k, v, o, kr, apply_rope=1, **kw)
         else:
             taa.apex_attn_prefill(q, kr, v, o, None, apply_rope=2, **kw)
-        if ev:
+        if samp_attn:
             ev[2].record()
 
     settle(torch, step)
@@ -164,12 +174,14 @@ def time_prefill(taa, torch, name, steps, warmup):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(evs[i])
+        step(i, evs[i])
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    rope_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
-    attn_min = min(e[1].elapsed_time(e[2]) for e in evs)
+    attn = [evs[i][1].elapsed_time(evs[i][2]) for i in range(0, steps, every)]
+    ropes = [evs[i][0].elapsed_time(evs[i][1]) for i in range(every // 2, steps, every)]
+    rope_ms = sum(ropes) / len(ropes)
+    attn_ms = sum(attn) / len(attn)
+    attn_min = min(attn)
     del q, k, v, kr, o
     return w, wall * 1e3, rope_ms, attn_ms, attn_min
 
@@ -411,6 +423,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "settle_s": SETTLE_S,
+        "event_sample": "per-launch events on 1 step in %d" % EVENT_EVERY,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
