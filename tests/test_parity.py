@@ -194,6 +194,39 @@ def test_prefill_yarn(taa, case):
     _check(o, ref, dtype, "prefill yarn %s" % (case,))
 
 
+# Scores built to move the running row max: every query's dim 0 is A and key
+# j's dim 0 is c * (j // 64), so in log2 units q.k / sqrt(d_h) steps by `jump`
+# from one 64-key tile to the next (past the kernels' lazy-rescale headroom of
+# 8 when |jump| > 8); the other dims carry a small noise. Inputs are given
+# rotated (apply_rope = 0) so the designed scores are the scores.
+GROW_CASES = [
+    # B, S, Hq, Hkv, d, W, jump, dtype
+    (1, 300, 4, 2, 128, 0, 9.0, "bf16"),     # the max moves on every tile
+    (1, 300, 4, 2, 128, 100, 9.0, "bf16"),   # ... inside a window that spans tiles
+    (1, 200, 4, 1, 64, 0, 9.0, "bf16"),
+    (1, 300, 4, 2, 128, 0, -9.0, "bf16"),    # falling scores: the first tile holds the max
+    (1, 300, 8, 2, 128, 0, 30.0, "bf16"),    # jumps far past the headroom
+    (1, 300, 4, 2, 128, 0, 9.0, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", GROW_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_running_max_moves(taa, case):
+    B, S, Hq, Hkv, d, W, jump, dtype = case
+    _say("prefill running max", case)
+    q, k, v = apex_inputs.prefill_inputs(B, S, Hq, Hkv, d, dtype, seed=77, device="cuda")
+    A = 8.0
+    c = jump * math.sqrt(d) / (A * math.log2(math.e))
+    q, k = q * 0.05, k * 0.05
+    q[..., 0] = A
+    k[..., 0] = (c * (torch.arange(S, device="cuda") // 64).float()).to(k.dtype)
+    o = torch.empty_like(q)
+    taa.apex_attn_prefill(q, k, v, o, None, causal=1, W=W, apply_rope=0)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), causal=1, W=W, apply_rope=0)
+    _check(o, ref, dtype, "prefill running max %s" % (case,))
+
+
 def test_k_rope_out_holds_rotated_keys_and_may_alias_k(taa):
     B, S, Hq, Hkv, d = 1, 200, 8, 2, 128
     q, k, v = apex_inputs.prefill_inputs(B, S, Hq, Hkv, d, "bf16", seed=5, device="cuda")
