@@ -186,25 +186,44 @@ def time_prefill(taa, torch, name, steps, warmup):
     return w, wall * 1e3, rope_ms, attn_ms, attn_min
 
 
+def time_calls(torch, fn, steps):
+    """Mean duration of `steps` back-to-back calls of fn, from one pair of
+    events around the whole loop, plus the per-call durations of a sample of
+    the calls (events around one call in EVENT_EVERY; every call of a short
+    run), all on the launch stream. Events around every call would add their
+    own ~3.5 us to short kernels."""
+    every = EVENT_EVERY if steps >= 2 * EVENT_EVERY else 1
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    e0, e1 = ev(), ev()
+    samples = [(ev(), ev()) for _ in range(0, steps, every)]
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(steps):
+        if i % every == 0:
+            samples[i // every][0].record()
+        fn()
+        if i % every == 0:
+            samples[i // every][1].record()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, sorted(a.elapsed_time(b) for a, b in samples)
+
+
 def time_rmsnorm(taa, torch, name, steps, warmup):
     import apex_inputs
     w = apex_inputs.WORKLOADS[name]
     x, g = apex_inputs.workload_inputs(name, device="cuda")
     y = torch.empty_like(x)
-    settle(torch, lambda: taa.apex_rmsnorm(x, g, y, eps=w["eps"]))
+
+    def call():
+        taa.apex_rmsnorm(x, g, y, eps=w["eps"])
+
+    settle(torch, call)
     for _ in range(warmup):
-        taa.apex_rmsnorm(x, g, y, eps=w["eps"])
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    torch.cuda.synchronize()
-    for a, b in evs:
-        a.record()
-        taa.apex_rmsnorm(x, g, y, eps=w["eps"])
-        b.record()
-    torch.cuda.synchronize()
-    ms = sorted(a.elapsed_time(b) for a, b in evs)
+        call()
+    mean, ms = time_calls(torch, call, steps)
     del x, g, y
-    return w, sum(ms) / len(ms), ms[0]
+    return w, mean, ms[0]
 
 
 def time_decode(taa, torch, steps, warmup, name=DECODE):
@@ -224,17 +243,9 @@ def time_decode(taa, torch, steps, warmup, name=DECODE):
     settle(torch, call)
     for _ in range(warmup):
         call()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    torch.cuda.synchronize()
-    for a, b in evs:
-        a.record()
-        call()
-        b.record()
-    torch.cuda.synchronize()
-    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    mean, ms = time_calls(torch, call, steps)
     del q, kc, vc, kn, vn, o, ws
-    return w, sum(ms) / len(ms), ms[len(ms) // 2], ms[0]
+    return w, mean, ms[len(ms) // 2], ms[0]
 
 
 def cpu_baseline(w, budget_s):
@@ -372,7 +383,8 @@ def main():
             "value": round(gbs, 1), "unit": "GB/s", "ms_per_call": round(d_mean, 4),
             "ms_median": round(d_med, 4), "ms_min": round(d_min, 4),
             "algorithmic_bytes": dbytes, "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "note": "whole call: split-K pass + combine pass, events on the launch stream"}
+            "note": ("whole call: split-K pass + combine pass; mean from events around the "
+                     "timed calls, median/min from per-call events on a sample of them")}
         torch.cuda.empty_cache()
         log("timing %s: %d warmup + %d calls" % (MLA_DECODE, args.warmup, dsteps))
         mw, m_mean, m_med, m_min = time_decode(taa, torch, dsteps, args.warmup, MLA_DECODE)
