@@ -72,17 +72,43 @@ int decode_splits(int B, int Hkv, int n_hb, int Sk) {
   return (int)want;
 }
 
+// Workgroups of an RMSNorm launch: every wave is resident from the start
+// and takes the same number of rows (grid-stride), so no second, partly
+// filled round of workgroups trails the first.
+template <typename K>
+long long rmsnorm_blocks(K kernel, long long rows) {
+  const long long waves_per_block = apex::kRmsThreads / 64;
+  int dev = 0, n_cu = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, apex::kRmsThreads, 0) !=
+          hipSuccess ||
+      n_cu < 1 || per_cu < 1) {
+    (void)hipGetLastError();
+    n_cu = 256;
+    per_cu = 4;
+  }
+  const long long resident = (long long)n_cu * per_cu * waves_per_block;
+  const long long rows_per_wave = (rows + resident - 1) / resident;
+  const long long waves = (rows + rows_per_wave - 1) / rows_per_wave;
+  return (waves + waves_per_block - 1) / waves_per_block;
+}
+
+template <typename T, int NC>
+void launch_rmsnorm_nc(const apex::RmsNormParams& p, hipStream_t st) {
+  const long long blocks = rmsnorm_blocks(apex::rmsnorm_kernel<T, NC>, p.rows);
+  hipLaunchKernelGGL((apex::rmsnorm_kernel<T, NC>), dim3((unsigned)blocks),
+                     dim3(apex::kRmsThreads), 0, st, p);
+}
+
 template <typename T>
 int launch_rmsnorm(const apex::RmsNormParams& p, int nc, hipStream_t st) {
-  long long blocks = (p.rows + 3) / 4;
-  if (blocks > 4096) blocks = 4096;  // grid-stride beyond 16 workgroups per CU
-  const dim3 grid((unsigned)blocks), block(apex::kRmsThreads);
   switch (nc) {
-    case 1: hipLaunchKernelGGL((apex::rmsnorm_kernel<T, 1>), grid, block, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((apex::rmsnorm_kernel<T, 2>), grid, block, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((apex::rmsnorm_kernel<T, 4>), grid, block, 0, st, p); break;
-    case 8: hipLaunchKernelGGL((apex::rmsnorm_kernel<T, 8>), grid, block, 0, st, p); break;
-    case 16: hipLaunchKernelGGL((apex::rmsnorm_kernel<T, 16>), grid, block, 0, st, p); break;
+    case 1: launch_rmsnorm_nc<T, 1>(p, st); break;
+    case 2: launch_rmsnorm_nc<T, 2>(p, st); break;
+    case 4: launch_rmsnorm_nc<T, 4>(p, st); break;
+    case 8: launch_rmsnorm_nc<T, 8>(p, st); break;
+    case 16: launch_rmsnorm_nc<T, 16>(p, st); break;
     default: return APEX_EUNSUPPORTED;
   }
   return launch_status();
