@@ -442,6 +442,29 @@ def test_decode_yarn(taa, ys):
     _check(o, ref, "bf16", "decode yarn %s" % ys)
 
 
+# Cached keys whose scores step by `jump` (log2 units) every 32 slots, so the
+# running max of every split part moves and the parts' maxima differ widely
+# before the log-sum-exp combine; q and the cache are given rotated.
+@pytest.mark.parametrize("jump", [9.0, -9.0, 30.0])
+def test_decode_running_max_moves(taa, jump):
+    B, Sk, Hq, Hkv, d = 2, 9000, 16, 2, 128
+    _say("decode running max", jump)
+    q, kc, vc, _, _ = _decode_inputs(B, Sk, Hq, Hkv, d, seed=91)
+    A = 8.0
+    c = jump * math.sqrt(d) / (A * math.log2(math.e))
+    q, kc = q * 0.05, kc * 0.05
+    q[..., 0] = A
+    steps = (torch.arange(Sk, device="cuda") // 32).float()
+    kc[..., 0] = (c * (steps - steps.max() / 2) / 10).to(kc.dtype)  # ramps over the cache
+    o = torch.empty_like(q)
+    ws = torch.empty(taa.apex_attn_decode_workspace_bytes(B, Hq, Hkv, Sk, d), dtype=torch.uint8,
+                     device="cuda")
+    taa.apex_attn_decode(q, kc, vc, None, None, o, m=Sk - 1, apply_rope=0, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.decode(q.cpu(), kc.cpu(), vc.cpu(), None, None, m=Sk - 1, apply_rope=0)
+    _check(o, ref, "bf16", "decode running max %s" % jump)
+
+
 def test_decode_repeat_is_idempotent(taa):
     B, Sk, Hq, Hkv, d = 2, 3000, 32, 2, 128
     q, kc, vc, kn, vn = _decode_inputs(B, Sk, Hq, Hkv, d, seed=77)
