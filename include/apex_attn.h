@@ -103,6 +103,10 @@ int apex_rope_qk(const void* q, const void* k, void* q_out, void* k_out, int B, 
  *   k_rope_out: [B, H_kv, S, d_h] receives RoPE(k) when apply_rope = 1 (the
  *     values a KV cache stores). It may equal k (in-place rotation) but must
  *     not overlap q, v or o.
+ * Precision with APEX_BF16: the matrix-core operands are bf16 -- the rotated
+ * keys, the rotated queries already multiplied by log2(e)/sqrt(d_h) (times the
+ * YaRN temperature), and the probabilities -- each rounded to nearest even
+ * once; scores, the softmax and the output sums are fp32.
  * Errors: APEX_EINVAL for H_q % H_kv != 0, sizes < 1, W < 0, W > 0 with
  * causal = 0, prefix < 0, prefix > 0 with causal = 0, m0 < 0, apply_rope not
  * 0/1/2, base <= 0 with apply_rope, yarn_s < 1 or not finite, a NULL
