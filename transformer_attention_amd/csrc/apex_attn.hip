@@ -65,8 +65,8 @@ int head_pack(int G) {
 // Split-K geometry of the decode: workgroups per (b, KV head, head block).
 int decode_splits(int B, int Hkv, int n_hb, int Sk) {
   const long long groups = (long long)B * Hkv * n_hb;
-  long long want = (1024 + groups - 1) / groups;        // about 4 workgroups per CU
-  const long long cap = (Sk + 4095) / 4096;             // >= 1024 keys per wave
+  long long want = (512 + groups - 1) / groups;         // about one wave per SIMD
+  const long long cap = (Sk + 2047) / 2048;             // >= 1024 keys per wave
   if (want > cap) want = cap;
   if (want < 1) want = 1;
   return (int)want;
