@@ -14,7 +14,8 @@
 //     loads 16 contiguous bytes of key l%16); Q^T stays in registers;
 //   - O^T += V^T P^T: each wave stages its 32-key V tile in its own LDS slice
 //     and reads it back transposed with ds_read_b64_tr_b16;
-//   - the next 32 keys' loads are issued before the current ones compute;
+//   - loads run two 32-key iterations ahead of the compute (two register
+//     buffers, so 32 KB per wave are in flight);
 //   - each part ends with its fp32 (running max, sum, unnormalised output) in
 //     the workspace; the combine kernel merges the parts of a query head with
 //     the log-sum-exp rule and writes the bf16 output.
@@ -135,8 +136,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
     }
   }
 
-  u32x4 kreg[2][KK], vreg[VCH];
-  auto load = [&](int base) {
+  // Two register buffers of loads in flight: the keys/values of iteration
+  // it + 2 are requested as soon as iteration it has taken its own out of
+  // the buffer they share (32 KB per wave in flight).
+  u32x4 kA[2][KK], vA[VCH], kB[2][KK], vB[VCH];
+  auto load = [&](int base, u32x4 (&kreg)[2][KK], u32x4 (&vreg)[VCH]) {
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) {
       const int key = base + kb * 16 + l16;
@@ -162,8 +166,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
   float m_run = kNegInf, l_run = 0.0f;
 
   const int n_it = part_hi >= part_lo ? (part_hi - part_lo) / kDecBN + 1 : 0;
-  if (n_it > 0) load(part_lo);
-  for (int it = 0; it < n_it; it++) {
+  if (n_it > 0) load(part_lo, kA, vA);
+  if (n_it > 1) load(part_lo + kDecBN, kB, vB);
+  auto iteration = [&](int it, u32x4 (&kreg)[2][KK], u32x4 (&vreg)[VCH]) {
     const int base = part_lo + it * kDecBN;
     u32x4 kcur[2][KK], vcur[VCH];
 #pragma unroll
@@ -172,7 +177,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
       for (int kk = 0; kk < KK; kk++) kcur[kb][kk] = kreg[kb][kk];
 #pragma unroll
     for (int c = 0; c < VCH; c++) vcur[c] = vreg[c];
-    if (it + 1 < n_it) load(base + kDecBN);
+    if (it + 2 < n_it) load(base + 2 * kDecBN, kreg, vreg);
 
     if (has_new && base <= m && m < base + kDecBN) {  // slot m from registers
       const int km = (int)(m - base);
@@ -250,7 +255,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  int it = 0;
+  for (; it + 1 < n_it; it += 2) {
+    iteration(it, kA, vA);
+    iteration(it + 1, kB, vB);
   }
+  if (it < n_it) iteration(it, kA, vA);
 
   // ---- partial result of this part ----
   float l_tot = l_run;
