@@ -665,3 +665,49 @@ def test_workload_rmsnorm(taa, name):
     torch.cuda.synchronize()
     ref = oracle.rmsnorm(x.cpu(), g.cpu(), eps=w["eps"])
     _check_rmsnorm(y, ref, w["dtype"], name)
+
+
+def test_calls_replay_from_a_hip_graph(taa):
+    # Every entry point only enqueues kernels on the caller's stream and
+    # allocates nothing, so a sequence of calls can be captured once and
+    # replayed; each replay must reproduce the eager results bit for bit.
+    B, S, Hq, Hkv, d = 1, 300, 8, 2, 128
+    q, k, v = apex_inputs.prefill_inputs(B, S, Hq, Hkv, d, "bf16", seed=21, device="cuda")
+    kr, o = torch.empty_like(k), torch.empty_like(q)
+    Sk = 2048
+    dq, kc, vc, kn, vn = _decode_inputs(2, Sk, 16, 2, d, seed=22)
+    od = torch.empty_like(dq)
+    ws = torch.empty(taa.apex_attn_decode_workspace_bytes(2, 16, 2, Sk, d), dtype=torch.uint8,
+                     device="cuda")
+    x = torch.randn(64, 512, device="cuda").to(torch.bfloat16)
+    gam = torch.ones(512, device="cuda").to(torch.bfloat16)
+    y = torch.empty_like(x)
+
+    def calls():
+        taa.apex_rope_qk(None, k, k_out=kr, m0=5)
+        taa.apex_attn_prefill(q, kr, v, o, None, causal=1, W=100, m0=5, apply_rope=2)
+        taa.apex_attn_decode(dq, kc, vc, None, None, od, m=Sk - 1, workspace=ws)
+        taa.apex_rmsnorm(x, gam, y)
+
+    calls()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (kr, o, od, y)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (kr, o, od, y):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip((kr, o, od, y), want):
+            assert torch.equal(got, ref), rep
+        calls()  # eager work between the replays
+        torch.cuda.synchronize()
