@@ -110,7 +110,9 @@ int apex_rope_qk(const void* q, const void* k, void* q_out, void* k_out, int B, 
  * Errors: APEX_EINVAL for H_q % H_kv != 0, sizes < 1, W < 0, W > 0 with
  * causal = 0, prefix < 0, prefix > 0 with causal = 0, m0 < 0, apply_rope not
  * 0/1/2, base <= 0 with apply_rope, yarn_s < 1 or not finite, a NULL
- * required pointer, an unknown dtype; APEX_EUNSUPPORTED for d_h not 64 or 128.
+ * required pointer, an unknown dtype; APEX_EUNSUPPORTED for d_h not 64 or 128,
+ * and for S * d_h * (element bytes) of 4 GiB or more (one head's rows are
+ * addressed with 32-bit byte offsets: S up to 16.7 million bf16 rows of 128).
  */
 int apex_attn_prefill(const void* q, const void* k, const void* v, void* o,
                       void* k_rope_out, int B, int S, int H_q, int H_kv, int d_h,
@@ -139,7 +141,8 @@ int apex_attn_prefill(const void* q, const void* k, const void* v, void* o,
  *   apex_attn_prefill (the YaRN frequencies follow d_r).
  * Built for bf16 with d_h = 128, d_r = 64.
  * Errors: as apex_attn_prefill, with d_h and d_r each even and >= 2
- * (APEX_EINVAL otherwise); APEX_EUNSUPPORTED for any other (d_h, d_r) or fp32.
+ * (APEX_EINVAL otherwise); APEX_EUNSUPPORTED for any other (d_h, d_r) or fp32,
+ * and for S * (d_h + d_r) * 2 bytes of 4 GiB or more.
  */
 int apex_attn_prefill_mla(const void* q, const void* k, const void* v, void* o,
                           void* k_rope_out, int B, int S, int H_q, int H_kv, int d_h,

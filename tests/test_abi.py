@@ -106,6 +106,14 @@ def test_prefill_rejects(L):
     assert _prefill(L, d=80) == EUNSUP
 
 
+def test_prefill_rejects_rows_beyond_32_bit_offsets(L):
+    # one head's rows are addressed with 32-bit byte offsets; checked before
+    # anything is launched, so the dummy pointers are never touched
+    assert _prefill(L, S=1 << 24, B=1, Hq=1, Hkv=1) == EUNSUP             # bf16, d_h 128
+    assert _prefill(L, S=1 << 24, d=64, dtype=0, Hq=1, Hkv=1) == EUNSUP  # fp32, d_h 64
+    assert _mla(L, S=(1 << 32) // 384 + 1, Hq=1, Hkv=1) == EUNSUP
+
+
 def test_prefill_rope_modes_and_rope_buffer(L):
     # k_rope_out is needed only when apply_rope = 1; other checks still apply.
     assert _prefill(L, kr=None, rope=0, Hq=3, Hkv=2) == EINVAL

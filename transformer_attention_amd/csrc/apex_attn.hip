@@ -204,6 +204,8 @@ int apex_attn_prefill(const void* q, const void* k, const void* v, void* o, void
     return APEX_EINVAL;
   const int dc = check_dims(d_h, dtype);
   if (dc != APEX_OK) return dc;
+  // the attention kernels address one head's rows with 32-bit byte offsets
+  if ((long long)S * d_h * (dtype == APEX_BF16 ? 2 : 4) > 0xffffffffLL) return APEX_EUNSUPPORTED;
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
 
@@ -274,6 +276,8 @@ int apex_attn_prefill_mla(const void* q, const void* k, const void* v, void* o,
     return APEX_EINVAL;
   if (dtype != APEX_F32 && dtype != APEX_BF16) return APEX_EINVAL;
   if (dtype != APEX_BF16 || d_h != 128 || d_r != 64) return APEX_EUNSUPPORTED;
+  // the attention kernel addresses one head's rows with 32-bit byte offsets
+  if ((long long)S * (d_h + d_r) * 2 > 0xffffffffLL) return APEX_EUNSUPPORTED;
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
 
