@@ -19,7 +19,9 @@
  *     Shape Convention"): element (b, h, s, t) sits at ((b*H + h)*S + s)*d_h + t.
  *   - dtype: APEX_F32 (fp32 storage and math) or APEX_BF16 (bf16 storage,
  *     fp32 softmax and accumulation, bf16 output rounded to nearest even).
- *   - Every pointer is a device pointer owned by the caller, 16-byte aligned.
+ *   - Every pointer is a device pointer owned by the caller, 16-byte aligned
+ *     (the kernels move every buffer in 16-byte pieces; a pointer that is not
+ *     is APEX_EINVAL).
  *     The library never allocates, frees or synchronizes; it keeps no mutable
  *     global state and is reentrant.
  *   - stream is a hipStream_t (NULL = the null stream). Every call only

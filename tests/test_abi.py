@@ -244,3 +244,21 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         taa.apex_rope_qk(q, None)
+
+
+def test_misaligned_pointers_are_rejected(L):
+    # every buffer is moved in 16-byte pieces, so each pointer argument must
+    # sit on that grid; checked before anything is launched
+    off = P + 8
+    for name in ("q", "k", "qo", "ko"):
+        assert _rope(L, **{name: off}) == EINVAL, name
+    for name in ("q", "k", "v", "o", "kr"):
+        assert _prefill(L, **{name: off}) == EINVAL, name
+        assert _mla(L, **{name: off}) == EINVAL, name
+    # k_rope_out is not checked when apply_rope != 1 (d_h 96 stops the call later)
+    assert _prefill(L, kr=off, rope=2, d=96) == EUNSUP
+    for name in ("q", "kc", "vc", "kn", "vn", "o", "ws"):
+        assert _decode(L, **{name: off}) == EINVAL, name
+        assert _decode_mla(L, **{name: off}) == EINVAL, name
+    for name in ("x", "g", "y"):
+        assert _rms(L, **{name: off}) == EINVAL, name

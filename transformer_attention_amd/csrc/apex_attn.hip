@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "apex_attn.h"
 #include "decode_kernel.hpp"
 #include "prefill_f32_kernel.hpp"
@@ -18,6 +20,14 @@ namespace {
 constexpr double kLog2e = 1.4426950408889634074;
 
 bool head_size_ok(int d_h) { return d_h == 64 || d_h == 128; }
+
+// The kernels move every buffer in 16-byte pieces; a pointer off that grid is
+// rejected (NULL passes, its own check decides).
+bool aligned16(std::initializer_list<const void*> ptrs) {
+  for (const void* ptr : ptrs)
+    if ((uintptr_t)ptr & 15u) return false;
+  return true;
+}
 
 // A YaRN scale factor: >= 1 and finite (1 = plain RoPE).
 bool yarn_ok(double s) { return s >= 1.0 && s <= 1e30; }
@@ -177,6 +187,7 @@ int apex_rope_qk(const void* q, const void* k, void* q_out, void* k_out, int B, 
                  void* stream) {
   if ((q == nullptr) != (q_out == nullptr) || (k == nullptr) != (k_out == nullptr) || (!q && !k))
     return APEX_EINVAL;
+  if (!aligned16({q, k, q_out, k_out})) return APEX_EINVAL;
   if (B < 1 || S < 1 || (q && H_q < 1) || (k && H_kv < 1) || m0 < 0 || !(base > 0.0) ||
       !yarn_ok(yarn_s))
     return APEX_EINVAL;
@@ -196,6 +207,7 @@ int apex_attn_prefill(const void* q, const void* k, const void* v, void* o, void
                       int64_t m0, double base, double yarn_s, int apply_rope, int dtype,
                       void* stream) {
   if (!q || !k || !v || !o || (apply_rope == 1 && !k_rope_out)) return APEX_EINVAL;
+  if (!aligned16({q, k, v, o, apply_rope == 1 ? k_rope_out : nullptr})) return APEX_EINVAL;
   if (B < 1 || S < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0) return APEX_EINVAL;
   if (W < 0 || (W > 0 && !causal) || (causal != 0 && causal != 1)) return APEX_EINVAL;
   if (prefix < 0 || (prefix > 0 && !causal)) return APEX_EINVAL;
@@ -267,6 +279,7 @@ int apex_attn_prefill_mla(const void* q, const void* k, const void* v, void* o,
                           int causal, int W, int prefix, int64_t m0, double base, double yarn_s,
                           int apply_rope, int dtype, void* stream) {
   if (!q || !k || !v || !o || (apply_rope == 1 && !k_rope_out)) return APEX_EINVAL;
+  if (!aligned16({q, k, v, o, apply_rope == 1 ? k_rope_out : nullptr})) return APEX_EINVAL;
   if (B < 1 || S < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0) return APEX_EINVAL;
   if (d_h < 2 || (d_h & 1) || d_r < 2 || (d_r & 1)) return APEX_EINVAL;
   if (W < 0 || (W > 0 && !causal) || (causal != 0 && causal != 1)) return APEX_EINVAL;
@@ -316,6 +329,7 @@ int apex_attn_prefill_mla(const void* q, const void* k, const void* v, void* o,
 int apex_rmsnorm(const void* x, const void* gamma, void* y, int64_t rows, int d, double eps,
                  int dtype, void* stream) {
   if (!x || !gamma || !y || rows < 1 || d < 1 || !(eps >= 0.0) || !(eps <= 1e30)) return APEX_EINVAL;
+  if (!aligned16({x, gamma, y})) return APEX_EINVAL;
   if (dtype != APEX_F32 && dtype != APEX_BF16) return APEX_EINVAL;
   if (d % 8 != 0 || d > 8192) return APEX_EUNSUPPORTED;
   hipStream_t st = (hipStream_t)stream;
@@ -341,6 +355,7 @@ int apex_attn_decode(const void* q, void* k_cache, void* v_cache, const void* k_
                      size_t workspace_bytes, int dtype, void* stream) {
   if (!q || !k_cache || !v_cache || !o || ((k_new == nullptr) != (v_new == nullptr)))
     return APEX_EINVAL;
+  if (!aligned16({q, k_cache, v_cache, k_new, v_new, o, workspace})) return APEX_EINVAL;
   if (B < 1 || Sk < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || W < 0) return APEX_EINVAL;
   if (m < 0 || m >= Sk || (apply_rope != 0 && apply_rope != 1) || (apply_rope && !(base > 0.0)) ||
       !yarn_ok(yarn_s))
@@ -365,6 +380,7 @@ int apex_attn_decode_mla(const void* q, void* k_cache, void* v_cache, const void
                          void* workspace, size_t workspace_bytes, int dtype, void* stream) {
   if (!q || !k_cache || !v_cache || !o || ((k_new == nullptr) != (v_new == nullptr)))
     return APEX_EINVAL;
+  if (!aligned16({q, k_cache, v_cache, k_new, v_new, o, workspace})) return APEX_EINVAL;
   if (B < 1 || Sk < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || W < 0) return APEX_EINVAL;
   if (d_h < 2 || (d_h & 1) || d_r < 2 || (d_r & 1)) return APEX_EINVAL;
   if (m < 0 || m >= Sk || (apply_rope != 0 && apply_rope != 1) || (apply_rope && !(base > 0.0)) ||
