@@ -140,15 +140,20 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
   // it + 2 are requested as soon as iteration it has taken its own out of
   // the buffer they share (32 KB per wave in flight).
   u32x4 kA[2][KK], vA[VCH], kB[2][KK], vB[VCH];
+  // Cache lines are read once, so the loads are marked non-temporal; the
+  // exception is measured: the 384-byte [content | rope] key rows of MLA read
+  // 1.5% faster as plain loads (their values stay non-temporal).
+  auto load_k = [](const u32x4* ptr) {
+    return DQK == DV ? __builtin_nontemporal_load(ptr) : *ptr;
+  };
   auto load = [&](int base, u32x4 (&kreg)[2][KK], u32x4 (&vreg)[VCH]) {
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) {
       const int key = base + kb * 16 + l16;
 #pragma unroll
       for (int kk = 0; kk < KK; kk++)
-        kreg[kb][kk] = key <= part_hi
-                           ? __builtin_nontemporal_load((const u32x4*)(kcb + (size_t)key * DQK + 32 * kk + 8 * g4))
-                           : u32x4{0, 0, 0, 0};
+        kreg[kb][kk] = key <= part_hi ? load_k((const u32x4*)(kcb + (size_t)key * DQK + 32 * kk + 8 * g4))
+                                      : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int c = 0; c < VCH; c++) {
