@@ -187,7 +187,9 @@ size_t apex_attn_decode_workspace_bytes(int B, int H_q, int H_kv, int Sk, int d_
  *   base, yarn_s: as for apex_attn_prefill (YaRN frequencies for q and k_new,
  *     the temperature on the scores when yarn_s > 1).
  *   workspace: device scratch of workspace_bytes >= the value returned by
- *     apex_attn_decode_workspace_bytes for the same sizes.
+ *     apex_attn_decode_workspace_bytes for the same sizes. Always required;
+ *     left untouched when the keys of a (b, KV head) are split in two parts
+ *     only (the two waves of one workgroup then merge them directly).
  * Errors: APEX_EINVAL for H_q % H_kv != 0, sizes < 1, W < 0, m < 0 or
  * m >= Sk, exactly one of k_new / v_new given, base <= 0 with apply_rope,
  * yarn_s < 1 or not finite, a NULL required pointer, an unknown dtype;

@@ -152,6 +152,8 @@ int launch_decode(const void* q, void* k_cache, void* v_cache, const void* k_new
   p.m = m; p.apply_rope = apply_rope;
   if (apply_rope) p.turns = apex::make_rope_turns(DR, base, yarn_s);
   p.n_hb = n_hb; p.n_parts = n_parts;
+  p.o = (uint16_t*)o;
+  p.fuse = n_split == 1;
   p.key_lo = (int)key_lo;
   p.keys_per_part = (int)kpp;
   // scores are q.k over all DQK dims
@@ -160,7 +162,7 @@ int launch_decode(const void* q, void* k_cache, void* v_cache, const void* k_new
   hipLaunchKernelGGL((apex::decode_split_kernel<DQK, DV, DR>), grid, dim3(apex::kDecThreads), 0,
                      st, p);
   const int rc = launch_status();
-  if (rc != APEX_OK) return rc;
+  if (rc != APEX_OK || p.fuse) return rc;
   apex::CombineParams c{p.ws_o, p.ws_ml, (uint16_t*)o, B * H_q, n_parts};
   hipLaunchKernelGGL(apex::decode_combine_kernel<DV>, dim3((B * H_q + 3) / 4), dim3(256), 0, st,
                      c);

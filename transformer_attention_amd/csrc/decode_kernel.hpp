@@ -51,6 +51,8 @@ struct DecodeParams {
   const uint16_t* vn;  // [B, Hkv, 1, DV] or null
   float* ws_o;         // [B*Hq, n_parts, DV]
   float* ws_ml;        // [B*Hq, n_parts, 2]
+  uint16_t* o;         // [B, Hq, 1, DV]: written here when fuse is set
+  int fuse;            // one split: the two waves merge their parts themselves
   int Sk, Hq, Hkv, G;
   long long m;
   RopeTurns turns;     // theta_i / (2 pi) of the DR / 2 rotated pairs (YaRN applied)
@@ -272,6 +274,44 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
   float l_tot = l_run;
   l_tot += __shfl_xor(l_tot, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
+  if (p.fuse) {
+    // With one split the workgroup's two waves hold the only two parts of
+    // their heads: they merge them by the log-sum-exp rule through LDS (each
+    // wave's own V slice, free after its last tile), and each writes the
+    // bf16 output of half of the dims. Lane layout as in O^T: dims
+    // 16db + 4g4 + r of head l16.
+    static_assert(kDecWaves == 2, "two parts per workgroup");
+    static_assert((DB * 64 * 4 + 2 * 64) * 4 <= kDecBN * VS * 2, "partials fit a V slice");
+    float* const mine = (float*)vlds[wave];
+    const float* const other = (const float*)vlds[wave ^ 1];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int db = 0; db < DB; db++) *(f32x4*)(mine + (db * 64 + lane) * 4) = oacc[db];
+    mine[DB * 256 + lane] = m_run;
+    mine[DB * 256 + 64 + lane] = l_tot;
+    __syncthreads();
+    const float m_o = other[DB * 256 + lane], l_o = other[DB * 256 + 64 + lane];
+    const float M = fmaxf(m_run, m_o);
+    const float w_me = m_run == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
+    const float w_o = m_o == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m_o - M);
+    const float inv = 1.0f / (w_me * l_tot + w_o * l_o);
+    if (head_ok) {
+      uint16_t* const orow = p.o + ((size_t)b * p.Hq + head) * DV;
+#pragma unroll
+      for (int db = 0; db < DB; db++)
+        if ((db < DB / 2) == (wave == 0)) {
+          const f32x4 oo = *(const f32x4*)(other + (db * 64 + lane) * 4);
+          u32x2 w;
+          w[0] = pack_bf16x2((w_me * oacc[db][0] + w_o * oo[0]) * inv,
+                             (w_me * oacc[db][1] + w_o * oo[1]) * inv);
+          w[1] = pack_bf16x2((w_me * oacc[db][2] + w_o * oo[2]) * inv,
+                             (w_me * oacc[db][3] + w_o * oo[3]) * inv);
+          *(u32x2*)(orow + 16 * db + 4 * g4) = w;
+        }
+    }
+    return;
+  }
   if (head_ok) {
     const size_t rec = ((size_t)b * p.Hq + head) * p.n_parts + part;
 #pragma unroll
