@@ -477,6 +477,26 @@ def test_decode_repeat_is_idempotent(taa):
     assert torch.equal(o1, o2)
 
 
+@pytest.mark.parametrize("Sk,fused", [(1500, True), (6000, False)])
+def test_decode_workspace_use_follows_the_split(taa, Sk, fused):
+    # With the keys of a (b, KV head) in two parts (one workgroup) the split
+    # pass merges them itself and leaves the workspace untouched; with more
+    # parts the partials go through the workspace to the combine kernel.
+    # Either way the output matches the oracle.
+    B, Hq, Hkv, d = 1, 16, 1, 128
+    q, kc, vc, kn, vn = _decode_inputs(B, Sk, Hq, Hkv, d, seed=91)
+    kc0, vc0 = kc.cpu(), vc.cpu()
+    ws = torch.full((taa.apex_attn_decode_workspace_bytes(B, Hq, Hkv, Sk, d),), 0x5A,
+                    dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    taa.apex_attn_decode(q, kc, vc, kn, vn, o, m=Sk - 1, workspace=ws)
+    torch.cuda.synchronize()
+    untouched = bool((ws == 0x5A).all().item())
+    assert untouched == fused
+    ref = oracle.decode(q.cpu(), kc0, vc0, kn.cpu(), vn.cpu(), m=Sk - 1)
+    _check(o, ref, "bf16", "decode Sk=%d, merged in the split pass: %s" % (Sk, fused))
+
+
 def test_decode_equals_last_prefill_row(taa):
     B, S, Hq, Hkv, d = 1, 1500, 32, 2, 128
     q, k, v = apex_inputs.prefill_inputs(B, S, Hq, Hkv, d, "bf16", seed=8, device="cuda")
