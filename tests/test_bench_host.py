@@ -47,3 +47,23 @@ def test_multi_gpu_request_is_refused():
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
                        text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_headline_is_the_largest_prefill_by_work():
+    # the line's value is quoted on the prefill workload with the most
+    # mask-adjusted FLOPs among the benchmark's prefill configurations
+    import apex_inputs
+    w = apex_inputs.WORKLOADS
+    cands = (bench.HEADLINE,) + bench.ROOFLINE_PREFILLS + (bench.TINY,)
+    assert max(cands, key=lambda n: bench.prefill_flops(w[n])) == bench.HEADLINE
+    assert bench.prefill_flops(w[bench.HEADLINE]) == 4 * 128 * 2 * 32 * 58722304
+
+
+def test_cpu_baseline_sample_counts_its_rows():
+    # the sample is one KV group of batch element 0: G heads x all S rows
+    import apex_inputs
+    w = apex_inputs.WORKLOADS[bench.HEADLINE]
+    G = w["Hq"] // w["Hkv"]
+    whole = bench.prefill_flops(w)
+    assert 4 * w["d"] * G * bench.n_visible(w["S"], w["causal"], w["W"]) * w["B"] * w["Hkv"] \
+        == whole

@@ -609,6 +609,41 @@ def test_yarn_mid_band_interpolation_formula():
         assert oracle.yarn_theta(th, s) == pytest.approx(th / (t * s + 1 - t), rel=1e-14)
 
 
+@pytest.mark.parametrize("s", [33.0, 64.0, 100.0, 1000.0, 65536.0])
+def test_yarn_mid_band_closed_form(s):
+    # With beta_slow = 1 the unclamped t = (lambda - 1) / (s - 1) makes the
+    # divisor t s + 1 - t = 1 + t (s - 1) equal to lambda itself, so across the
+    # band 32 <= lambda <= s the frequency becomes theta / lambda
+    # = theta^2 / (2 pi): a closed form that does not restate the interpolation
+    # (Part 1, §5.4, with the §5.3 defaults).
+    lams = np.concatenate([[32.0, 40.0, s - 0.1, s], np.geomspace(32.0, s, 200)])
+    for lam in lams[lams <= s]:
+        th = 2 * math.pi / lam
+        assert oracle.yarn_theta(th, s) == pytest.approx(th * th / (2 * math.pi), rel=1e-13)
+
+
+@pytest.mark.parametrize("s", [64.0, 1000.0])
+def test_yarn_band_edges(s):
+    # continuity where the band meets the low-frequency regime (lambda = beta_slow s):
+    # both sides give theta / s there
+    for eps in (1e-9, 1e-6, 1e-3):
+        lo, hi = 2 * math.pi / (s - eps), 2 * math.pi / (s + eps)
+        # a continuous theta' / theta moves by about eps / s^2 over a step of eps
+        assert abs(oracle.yarn_theta(lo, s) / lo - 1 / s) <= 2 * eps / s ** 2 + 1e-15
+        assert oracle.yarn_theta(hi, s) / hi == pytest.approx(1 / s, rel=1e-15)
+    # at the high-frequency edge (lambda = beta_fast = 32) the table's regimes
+    # meet with a jump whenever s > 32: just below it theta is kept, at it the
+    # divisor is already lambda = 32
+    below, at = 2 * math.pi / (32 - 1e-9), 2 * math.pi / 32
+    assert oracle.yarn_theta(below, s) == below
+    assert oracle.yarn_theta(at, s) / at == pytest.approx(1 / 32, rel=1e-13)
+    # theta' / theta never increases with the wavelength inside the band
+    lams = np.geomspace(32.0, s, 300)
+    ratio = [oracle.yarn_theta(2 * math.pi / l, s) * l / (2 * math.pi) for l in lams]
+    assert all(b <= a * (1 + 1e-15) for a, b in zip(ratio, ratio[1:]))
+    assert ratio[0] == pytest.approx(1 / 32, rel=1e-13) and ratio[-1] == pytest.approx(1 / s)
+
+
 @pytest.mark.parametrize("s", [4.0, 64.0])
 def test_yarn_prefill_matches_torch_sdpa(s):
     # RoPE with the YaRN frequencies as a complex rotation, then torch's SDPA
