@@ -202,6 +202,33 @@ int apex_attn_decode(const void* q, void* k_cache, void* v_cache,
                      double base, double yarn_s, int apply_rope, void* workspace,
                      size_t workspace_bytes, int dtype, void* stream);
 
+/* Bytes of the library's own decode scratch per GPU (apex_attn_decode_noalloc). */
+#define APEX_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * apex_attn_decode_noalloc -- apex_attn_decode for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, results and errors as
+ * apex_attn_decode, without the workspace: the split-K partial results go to
+ * a scratch array inside the library, APEX_DECODE_SCRATCH_BYTES (16 MiB) on
+ * each GPU it runs on, held until the process ends. The call allocates
+ * nothing; its first call on a device looks up that device's scratch address.
+ *   Sizes whose apex_attn_decode_workspace_bytes exceeds
+ *   APEX_DECODE_SCRATCH_BYTES return APEX_EWORKSPACE (the decode workload,
+ *   B = 64, H_q = 128, H_kv = 8, Sk = 32768, d_h = 128, needs 8.5 MB).
+ *   Nothing in the scratch has to start at zero: every partial result the
+ *   merge reads is written by the same call. Every call on one GPU shares
+ *   that GPU's scratch, so calls that overlap on one GPU (on different
+ *   streams, or from different threads) race on it; calls in one stream's
+ *   order do not. Errors: as apex_attn_decode, plus APEX_EHIP when the
+ *   scratch address cannot be obtained.
+ */
+int apex_attn_decode_noalloc(const void* q, void* k_cache, void* v_cache,
+                             const void* k_new, const void* v_new, void* o,
+                             int B, int Sk, int H_q, int H_kv, int d_h, int W, int64_t m,
+                             double base, double yarn_s, int apply_rope, int dtype,
+                             void* stream);
+
 /*
  * apex_attn_decode_mla -- apex_attn_decode for MLA with decoupled RoPE
  * (Part 2, §9.3): query and cached key rows are [content (d_h) | rope (d_r)],

@@ -30,8 +30,10 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["apex_attn_decode", "apex_attn_decode_mla",
-                                    "apex_attn_decode_workspace_bytes", "apex_attn_prefill", "apex_attn_prefill_mla", "apex_rmsnorm",
-                                    "apex_rope_qk", "apex_strerror"]
+                                    "apex_attn_decode_noalloc",
+                                    "apex_attn_decode_workspace_bytes", "apex_attn_prefill",
+                                    "apex_attn_prefill_mla", "apex_rmsnorm", "apex_rope_qk",
+                                    "apex_strerror"]
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -190,6 +192,36 @@ def test_decode_rejects(L):
     assert _decode(L, dtype=0) == EUNSUP    # decode is built for bf16 caches
     assert _decode(L, ws=None) == EWS
     assert _decode(L, wsb=16) == EWS
+
+
+def _decode_noalloc(L, q=P, kc=P, vc=P, kn=P, vn=P, o=P, B=2, Sk=64, Hq=16, Hkv=1, d=128, W=0,
+                    m=63, base=1e4, yarn=1.0, rope=1, dtype=1):
+    return L.apex_attn_decode_noalloc(q, kc, vc, kn, vn, o, B, Sk, Hq, Hkv, d, W, m, base, yarn,
+                                      rope, dtype, None)
+
+
+def test_decode_noalloc_rejects(L):
+    for kw in (dict(q=None), dict(kc=None), dict(vc=None), dict(o=None)):
+        assert _decode_noalloc(L, **kw) == EINVAL, kw
+    assert _decode_noalloc(L, kn=None) == EINVAL
+    assert _decode_noalloc(L, Hq=12, Hkv=8) == EINVAL
+    assert _decode_noalloc(L, B=0) == EINVAL
+    assert _decode_noalloc(L, W=-1) == EINVAL
+    assert _decode_noalloc(L, m=64) == EINVAL
+    assert _decode_noalloc(L, base=0.0) == EINVAL
+    assert _decode_noalloc(L, yarn=0.5) == EINVAL
+    assert _decode_noalloc(L, rope=2) == EINVAL
+    assert _decode_noalloc(L, dtype=4) == EINVAL
+    assert _decode_noalloc(L, d=9) == EINVAL
+    assert _decode_noalloc(L, d=96) == EUNSUP
+    assert _decode_noalloc(L, dtype=0) == EUNSUP
+    for name in ("q", "kc", "vc", "kn", "vn", "o"):
+        assert _decode_noalloc(L, **{name: P + 8}) == EINVAL, name
+    # partial results beyond the 16 MiB scratch are refused before any launch
+    ws = L.apex_attn_decode_workspace_bytes
+    assert ws(64, 128, 8, 32768, 128) <= 16 << 20   # the decode workload fits
+    assert ws(128, 256, 8, 32768, 128) > 16 << 20
+    assert _decode_noalloc(L, B=128, Sk=32768, Hq=256, Hkv=8, m=100) == EWS
 
 
 def _decode_mla(L, q=P, kc=P, vc=P, kn=P, vn=P, o=P, B=2, Sk=64, Hq=16, Hkv=1, d=128, dr=64,

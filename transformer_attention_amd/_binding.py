@@ -51,6 +51,9 @@ def lib():
         L.apex_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
                                        dbl, dbl, i32, vp, sz, i32, vp]
         L.apex_attn_decode.restype = i32
+        L.apex_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                               i32, i64, dbl, dbl, i32, i32, vp]
+        L.apex_attn_decode_noalloc.restype = i32
         L.apex_attn_decode_mla.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                            i32, i64, dbl, dbl, i32, vp, sz, i32, vp]
         L.apex_attn_decode_mla.restype = i32
@@ -166,6 +169,18 @@ def apex_attn_decode(q, k_cache, v_cache, k_new, v_new, o, m, W=0, base=10000.0,
                                   float(yarn_s), int(apply_rope), _ptr(workspace), nbytes,
                                   _dtype_code(q),
                                   _stream(q, stream)))
+
+
+def apex_attn_decode_noalloc(q, k_cache, v_cache, k_new, v_new, o, m, W=0, base=10000.0,
+                             apply_rope=1, stream=None, yarn_s=1.0):
+    """apex_attn_decode with the library's own scratch instead of a workspace."""
+    B, Hq, _, d = q.shape
+    Hkv, Sk = k_cache.shape[1], k_cache.shape[2]
+    _check("apex_attn_decode_noalloc",
+           lib().apex_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new),
+                                          _ptr(v_new), _ptr(o), B, Sk, Hq, Hkv, d, int(W), int(m),
+                                          float(base), float(yarn_s), int(apply_rope),
+                                          _dtype_code(q), _stream(q, stream)))
 
 
 def apex_attn_decode_mla(q, k_cache, v_cache, k_new, v_new, o, m, W=0, base=10000.0,

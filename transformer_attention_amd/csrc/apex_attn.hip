@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "apex_attn.h"
 #include "decode_kernel.hpp"
@@ -167,6 +168,42 @@ int launch_decode(const void* q, void* k_cache, void* v_cache, const void* k_new
   hipLaunchKernelGGL(apex::decode_combine_kernel<DV>, dim3((B * H_q + 3) / 4), dim3(256), 0, st,
                      c);
   return launch_status();
+}
+
+// Scratch of apex_attn_decode_noalloc: the split-K partial results live in
+// this file-scope device array instead of a caller workspace. Each GPU the
+// library runs on holds its own copy at its own address until the process
+// ends. In host code `scratch` is only a stand-in symbol, never a device
+// address: the address comes from hipGetSymbolAddress, once per device with
+// that device current, and only that address reaches kernels.
+static __device__ __align__(256) unsigned char scratch[APEX_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the device that owns `st` (the current device for
+// the null stream), looked up on the first call for that device.
+int scratch_address(hipStream_t st, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return APEX_EHIP;
+  int dev = cur;
+  if (st != nullptr && hipStreamGetDevice(st, &dev) != hipSuccess) return APEX_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return APEX_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return APEX_EHIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return APEX_EHIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return APEX_OK;
 }
 
 }  // namespace
@@ -374,6 +411,33 @@ int apex_attn_decode(const void* q, void* k_cache, void* v_cache, const void* k_
                                         (hipStream_t)stream);
   return launch_decode<64, 64, 64>(q, k_cache, v_cache, k_new, v_new, o, B, Sk, H_q, H_kv, W, m,
                                    base, yarn_s, apply_rope, workspace, (hipStream_t)stream);
+}
+
+int apex_attn_decode_noalloc(const void* q, void* k_cache, void* v_cache, const void* k_new,
+                             const void* v_new, void* o, int B, int Sk, int H_q, int H_kv,
+                             int d_h, int W, int64_t m, double base, double yarn_s,
+                             int apply_rope, int dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !o || ((k_new == nullptr) != (v_new == nullptr)))
+    return APEX_EINVAL;
+  if (!aligned16({q, k_cache, v_cache, k_new, v_new, o})) return APEX_EINVAL;
+  if (B < 1 || Sk < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || W < 0) return APEX_EINVAL;
+  if (m < 0 || m >= Sk || (apply_rope != 0 && apply_rope != 1) || (apply_rope && !(base > 0.0)) ||
+      !yarn_ok(yarn_s))
+    return APEX_EINVAL;
+  const int dc = check_dims(d_h, dtype);
+  if (dc != APEX_OK) return dc;
+  if (dtype != APEX_BF16) return APEX_EUNSUPPORTED;
+  if (apex_attn_decode_workspace_bytes(B, H_q, H_kv, Sk, d_h) > APEX_DECODE_SCRATCH_BYTES)
+    return APEX_EWORKSPACE;
+  if (B > 65535) return APEX_EUNSUPPORTED;
+  void* ws = nullptr;
+  const int rc = scratch_address((hipStream_t)stream, &ws);
+  if (rc != APEX_OK) return rc;
+  if (d_h == 128)
+    return launch_decode<128, 128, 128>(q, k_cache, v_cache, k_new, v_new, o, B, Sk, H_q, H_kv,
+                                        W, m, base, yarn_s, apply_rope, ws, (hipStream_t)stream);
+  return launch_decode<64, 64, 64>(q, k_cache, v_cache, k_new, v_new, o, B, Sk, H_q, H_kv, W, m,
+                                   base, yarn_s, apply_rope, ws, (hipStream_t)stream);
 }
 
 int apex_attn_decode_mla(const void* q, void* k_cache, void* v_cache, const void* k_new,
