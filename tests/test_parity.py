@@ -130,6 +130,16 @@ PREFILL_CASES = [
     (1, 777, 6, 1, 128, 0, 0, 0, "bf16", 1),
     (2, 700, 32, 8, 128, 1, 0, 0, "bf16", 0),
     (1, 640, 64, 8, 128, 1, 128, 0, "bf16", 1),
+    # d_h = 128 with heads packed 4 to a workgroup: S = 1 and 2, non-causal,
+    # W = 1, G = 16, positions near 65535
+    (1, 1, 4, 1, 128, 1, 0, 0, "bf16", 1),
+    (1, 2, 8, 1, 128, 1, 0, 3, "bf16", 1),
+    (1, 129, 4, 1, 128, 0, 0, 0, "bf16", 1),
+    (3, 333, 12, 3, 128, 1, 1, 0, "bf16", 1),
+    (1, 100, 32, 2, 128, 1, 0, 0, "bf16", 1),
+    (2, 96, 16, 4, 128, 0, 0, 0, "bf16", 0),
+    (1, 1000, 64, 4, 128, 1, 0, 0, "bf16", 1),
+    (1, 577, 8, 1, 128, 1, 200, 65535 - 600, "bf16", 1),
     (1, 128, 4, 2, 64, 1, 0, 0, "f32", 1),
     (1, 77, 4, 1, 128, 1, 9, 5, "f32", 1),
     (2, 33, 2, 2, 64, 0, 0, 0, "f32", 1),
@@ -159,6 +169,8 @@ PREFIX_CASES = [
     (1, 257, 4, 1, 128, 16, 1, "bf16"),      # P = 1: the causal mask
     (1, 1000, 32, 8, 128, 300, 520, "bf16"),
     (1, 640, 64, 8, 128, 128, 64, "bf16"),
+    (1, 500, 16, 2, 128, 50, 77, "bf16"),
+    (1, 70, 4, 1, 128, 0, 70, "bf16"),
     (1, 130, 4, 2, 64, 0, 45, "f32"),
     (1, 77, 4, 1, 128, 9, 20, "f32"),
 ]
@@ -213,6 +225,10 @@ GROW_CASES = [
     (1, 300, 4, 2, 128, 0, -9.0, "bf16"),    # falling scores: the first tile holds the max
     (1, 300, 8, 2, 128, 0, 30.0, "bf16"),    # jumps far past the headroom
     (1, 300, 4, 2, 128, 0, 9.0, "f32"),
+    (1, 300, 8, 2, 128, 0, 9.0, "bf16"),     # 4 heads per workgroup: rising,
+    (1, 300, 16, 2, 128, 100, 9.0, "bf16"),  # ... in a window,
+    (1, 300, 8, 2, 128, 0, -9.0, "bf16"),    # ... falling,
+    (1, 300, 32, 4, 128, 0, 30.0, "bf16"),   # ... far past the headroom
 ]
 
 
