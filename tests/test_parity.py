@@ -4,15 +4,15 @@ Inputs are seeded N(0,1) draws (apex_inputs) made on the GPU; the oracle gets
 exact CPU copies of the same inputs. Bars (per element):
   fp32 workloads: max |gpu - oracle| <= 1e-4
   bf16 workloads: max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3
-Small shapes are compared on every output element. The five benchmark
-workloads (tiny fp32 prefill, GQA causal prefill S=2048, window prefill
-S=16384 W=4096, local prefill S=65536 W=512, decode Sk=32768) are run at full
-size in the launch configuration the benchmark times and compared on every
-output element, streamed one KV group of (batch element, heads) at a time so
-the fp64 reference never holds a whole output; the larger ones are split into
-parts so that each test stays under a minute on the host cores. The other
-full-size workloads are compared on sampled rows (tile edges, first/last rows
-and heads, random rows).
+Small shapes are compared on every output element. Every benchmark workload
+(tiny fp32 prefill, GQA causal prefill S=2048, window prefill S=16384 W=4096,
+local prefill S=65536 W=512, GQA decode Sk=32768, and the prefix, YaRN and MLA
+prefills and the MLA decode) is run at full size in the launch configuration
+the benchmark times and compared on every output element, streamed one KV
+group of (batch element, heads) at a time so the fp64 reference never holds a
+whole output; the larger ones are split into parts so that each test stays
+under a minute on the host cores. Samplers of tile-edge, first/last and random
+rows run beside some of them as quicker checks.
 """
 import math
 import sys
@@ -382,12 +382,18 @@ def _run_prefill_workload_full(taa, name, part=0, nparts=1):
     w = apex_inputs.WORKLOADS[name]
     _say("workload", name, "part %d/%d" % (part + 1, nparts), w)
     q, k, v = apex_inputs.workload_inputs(name, device="cuda")
-    o, kr = torch.empty_like(q), torch.empty_like(k)
+    B, Hq, S, _ = q.shape
+    mla = w["kind"] == "mla_prefill"
+    o = torch.empty(B, Hq, S, v.shape[3], dtype=q.dtype, device="cuda")
+    kr = torch.empty_like(k)
     P, ys = w.get("prefix", 0), w.get("yarn_s", 1.0)
-    taa.apex_attn_prefill(q, k, v, o, kr, causal=w["causal"], W=w["W"], m0=w["m0"],
-                          base=w["base"], apply_rope=1, prefix=P, yarn_s=ys)
+    if mla:
+        taa.apex_attn_prefill_mla(q, k, v, o, kr, causal=w["causal"], W=w["W"], m0=w["m0"],
+                                  base=w["base"])
+    else:
+        taa.apex_attn_prefill(q, k, v, o, kr, causal=w["causal"], W=w["W"], m0=w["m0"],
+                              base=w["base"], apply_rope=1, prefix=P, yarn_s=ys)
     torch.cuda.synchronize()
-    B, Hq, S, d = q.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
     chunks = [(b, g) for b in range(B) for g in range(Hkv)][part::nparts]
@@ -396,8 +402,12 @@ def _run_prefill_workload_full(taa, name, part=0, nparts=1):
         qc, kc, vc = (x[b:b + 1].cpu() for x in (q, k, v))
         heads = range(g * G, (g + 1) * G)
         rows = np.array([h * S + i for h in heads for i in range(S)], dtype=np.int64)
-        ref = oracle.prefill(qc, kc, vc, causal=w["causal"], W=w["W"], m0=w["m0"],
-                             base=w["base"], rows=rows, prefix=P, yarn_s=ys)
+        if mla:
+            ref = oracle.prefill_mla(qc, kc, vc, w["d_r"], causal=w["causal"], W=w["W"],
+                                     m0=w["m0"], base=w["base"], rows=rows)
+        else:
+            ref = oracle.prefill(qc, kc, vc, causal=w["causal"], W=w["W"], m0=w["m0"],
+                                 base=w["base"], rows=rows, prefix=P, yarn_s=ys)
         stats.add(o[b, g * G:(g + 1) * G], ref, "%s b %d group %d" % (name, b, g))
     stats.check(w["dtype"], "%s part %d/%d (%d chunks of %d heads x %d rows)"
                 % (name, part + 1, nparts, len(chunks), G, S))
@@ -425,7 +435,12 @@ def test_workload_local_prefill_s65536_w512(taa, part):
     _run_prefill_workload_full(taa, "local_prefill_s65536_w512", part, 4)
 
 
-def test_workload_yarn_local_prefill_s32768_w4096_s4(taa):
+@pytest.mark.parametrize("part", range(4))
+def test_workload_yarn_local_prefill_s32768_w4096_s4(taa, part):
+    _run_prefill_workload_full(taa, "yarn_local_prefill_s32768_w4096_s4", part, 4)
+
+
+def test_workload_yarn_local_prefill_s32768_w4096_s4_sampled(taa):
     _run_prefill_workload(taa, "yarn_local_prefill_s32768_w4096_s4", 2000)
 
 
@@ -433,11 +448,21 @@ def test_workload_prefix_prefill_s2048_p512(taa):
     _run_prefill_workload_full(taa, "prefix_prefill_s2048_p512")
 
 
-def test_workload_prefix_local_prefill_s16384_w4096_p1024(taa):
+@pytest.mark.parametrize("part", range(4))
+def test_workload_prefix_local_prefill_s16384_w4096_p1024(taa, part):
+    _run_prefill_workload_full(taa, "prefix_local_prefill_s16384_w4096_p1024", part, 4)
+
+
+def test_workload_prefix_local_prefill_s16384_w4096_p1024_sampled(taa):
     _run_prefill_workload(taa, "prefix_local_prefill_s16384_w4096_p1024", 1500)
 
 
-def test_workload_mla_global_prefill_s16384(taa):
+@pytest.mark.parametrize("part", range(8))
+def test_workload_mla_global_prefill_s16384(taa, part):
+    _run_prefill_workload_full(taa, "mla_global_prefill_s16384", part, 8)
+
+
+def test_workload_mla_global_prefill_s16384_sampled(taa):
     name = "mla_global_prefill_s16384"
     w = apex_inputs.WORKLOADS[name]
     _say("workload", name, w)
@@ -689,19 +714,22 @@ def test_workload_mla_global_decode_sk32768(taa):
     q, kc, vc, kn, vn = apex_inputs.workload_inputs(name, device="cuda")
     B, Hq = q.shape[:2]
     Hkv, Sk = kc.shape[1], kc.shape[2]
-    bs = [0, 29, B - 1]
-    saved = [(kc[b].cpu(), vc[b].cpu()) for b in bs]
     o = torch.empty(B, Hq, 1, w["d"], dtype=q.dtype, device="cuda")
     ws = torch.empty(taa.apex_attn_decode_workspace_bytes(B, Hq, Hkv, Sk, w["d"]),
                      dtype=torch.uint8, device="cuda")
     taa.apex_attn_decode_mla(q, kc, vc, kn, vn, o, m=w["m"], W=w["W"], base=w["base"],
                              workspace=ws)
     torch.cuda.synchronize()
-    for b, (kcb, vcb) in zip(bs, saved):
-        ref = oracle.decode_mla(q[b:b + 1].cpu(), kcb[None], vcb[None], kn[b:b + 1].cpu(),
-                                vn[b:b + 1].cpu(), m=w["m"], d_r=w["d_r"], W=w["W"],
-                                base=w["base"])
-        _check(o[b:b + 1], ref, "bf16", "%s batch %d (all %d heads)" % (name, b, Hq))
+    # Every batch element, all heads; as for the GQA decode, the caches read back
+    # after the call differ from the inputs only in slot m, which the oracle
+    # takes from k_new / v_new.
+    stats = _Stats()
+    for b in range(B):
+        ref = oracle.decode_mla(q[b:b + 1].cpu(), kc[b:b + 1].cpu(), vc[b:b + 1].cpu(),
+                                kn[b:b + 1].cpu(), vn[b:b + 1].cpu(), m=w["m"], d_r=w["d_r"],
+                                W=w["W"], base=w["base"])
+        stats.add(o[b:b + 1], ref, "%s batch %d" % (name, b))
+    stats.check("bf16", "%s (all %d batch elements x %d heads)" % (name, B, Hq))
 
 
 # -------------------------------------------------------------- RMSNorm ----
