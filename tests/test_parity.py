@@ -480,6 +480,60 @@ def test_workload_mla_global_prefill_s16384_sampled(taa):
     _check(got, ref, w["dtype"], "%s (%d sampled rows)" % (name, rows.size))
 
 
+# ------------------------------------------ offsets past 2 GiB per head ----
+BIG_S = 12_000_000  # one head of 256-byte rows spans 3.07 GB; rows past 2**23 lie beyond 2**31 bytes
+
+
+def test_prefill_rows_beyond_2_gib_in_one_head(taa):
+    # The prefill addresses a head's rows through 32-bit buffer offsets, which
+    # must stay unsigned up to the 4 GiB the boundary accepts; RoPE runs at
+    # positions up to 12e6. With a 64-key window a row depends only on the 64
+    # rows up to it, so the oracle runs on short slices around rows on both
+    # sides of byte offset 2**31 (m0 = the slice's first row).
+    S, W, d = BIG_S, 64, 128
+    _say("prefill beyond 2 GiB per head", S, W)
+    q, k, v = apex_inputs.prefill_inputs(1, S, 1, 1, d, "bf16", seed=91, device="cuda")
+    o, kr = torch.empty_like(q), torch.empty_like(k)
+    taa.apex_attn_prefill(q, k, v, o, kr, causal=1, W=W, apply_rope=1)
+    torch.cuda.synchronize()
+    stats = _Stats()
+    for c in (100, 4_000_000, (1 << 23) - 1, 1 << 23, (1 << 23) + 1, 10_000_000, S - 1):
+        lo, hi = max(0, c - 255), min(S, c + 129)
+        ref = oracle.prefill(q[:, :, lo:hi].cpu(), k[:, :, lo:hi].cpu(), v[:, :, lo:hi].cpu(),
+                             causal=1, W=W, m0=lo)
+        first = 0 if lo == 0 else W - 1  # rows whose whole window lies in the slice
+        stats.add(o[:, :, lo + first:hi], ref[:, :, first:], "rows %d..%d" % (lo + first, hi - 1))
+        # the rotated keys written out at these positions
+        x = k[0, 0, c].cpu().double().numpy()
+        want = oracle.rope_row(x, c)
+        got = kr[0, 0, c].cpu().double().numpy()
+        assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -8 + 1e-6), c
+    stats.check("bf16", "prefill S=%d W=%d around byte offset 2**31" % (S, W))
+
+
+@pytest.mark.parametrize("m", [(1 << 23) + 10, BIG_S - 1])
+def test_decode_slots_beyond_2_gib_in_one_head(taa, m):
+    # A cache of 12e6 slots per (b, KV head); with a 64-slot window the visible
+    # slots m-63 .. m straddle byte offset 2**31 (m = 2**23 + 10) or lie past it.
+    # Without RoPE (inputs taken as already rotated) positions drop out of the
+    # arithmetic, so the oracle runs on the visible slice alone.
+    Sk, W, d, Hq = BIG_S, 64, 128, 16
+    _say("decode beyond 2 GiB per head", Sk, W, m)
+    q, kc, vc, kn, vn = apex_inputs.decode_inputs(1, Sk, Hq, 1, d, "bf16", seed=92,
+                                                  device="cuda")
+    lo = m - W + 1
+    kc0, vc0 = kc[:, :, lo:m + 1].cpu(), vc[:, :, lo:m + 1].cpu()
+    o = torch.empty_like(q)
+    ws = torch.empty(taa.apex_attn_decode_workspace_bytes(1, Hq, 1, Sk, d), dtype=torch.uint8,
+                     device="cuda")
+    taa.apex_attn_decode(q, kc, vc, kn, vn, o, m=m, W=W, apply_rope=0, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.decode(q.cpu(), kc0, vc0, kn.cpu(), vn.cpu(), m=W - 1, W=W, apply_rope=False)
+    _check(o, ref, "bf16", "decode Sk=%d W=%d m=%d" % (Sk, W, m))
+    assert torch.equal(kc[:, :, m], kn[:, :, 0]) and torch.equal(vc[:, :, m], vn[:, :, 0])
+    assert torch.equal(kc[:, :, lo:m].cpu(), kc0[:, :, :-1])  # the other visible slots untouched
+
+
 # --------------------------------------------------------------- decode ----
 DECODE_CASES = [
     # B, Sk, Hq, Hkv, d, W, m, with_new, apply_rope
