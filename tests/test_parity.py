@@ -511,6 +511,50 @@ def test_prefill_rows_beyond_2_gib_in_one_head(taa):
     stats.check("bf16", "prefill S=%d W=%d around byte offset 2**31" % (S, W))
 
 
+def test_prefill_mla_rows_beyond_2_gib_in_one_head(taa):
+    # MLA key rows are 384 bytes, so one head of 8e6 rows spans 3.07 GB and rows
+    # past 5,592,405 lie beyond byte offset 2**31; windowed, checked on slices.
+    S, W = 8_000_000, 64
+    _say("mla prefill beyond 2 GiB per head", S, W)
+    q, k, v = apex_inputs.mla_prefill_inputs(1, S, 1, 1, 128, 64, "bf16", seed=93, device="cuda")
+    o = torch.empty(1, 1, S, 128, dtype=q.dtype, device="cuda")
+    kr = torch.empty_like(k)
+    taa.apex_attn_prefill_mla(q, k, v, o, kr, causal=1, W=W)
+    torch.cuda.synchronize()
+    edge = (1 << 31) // 384
+    stats = _Stats()
+    for c in (100, 3_000_000, edge - 1, edge, edge + 1, S - 1):
+        lo, hi = max(0, c - 255), min(S, c + 129)
+        ref = oracle.prefill_mla(q[:, :, lo:hi].cpu(), k[:, :, lo:hi].cpu(), v[:, :, lo:hi].cpu(),
+                                 64, causal=1, W=W, m0=lo)
+        first = 0 if lo == 0 else W - 1
+        stats.add(o[:, :, lo + first:hi], ref[:, :, first:], "rows %d..%d" % (lo + first, hi - 1))
+        x = k[0, 0, c].cpu().double().numpy()
+        got = kr[0, 0, c].cpu().double().numpy()
+        assert np.array_equal(got[:128], x[:128]), c  # the content part is copied
+        want = oracle.rope_row(x[128:], c)
+        assert np.all(np.abs(got[128:] - want) <= np.abs(want) * 2.0 ** -8 + 1e-6), c
+    stats.check("bf16", "mla prefill S=%d W=%d around byte offset 2**31" % (S, W))
+
+
+def test_prefill_f32_rows_beyond_2_gib_in_one_head(taa):
+    # The fp32 path: one head of 12e6 rows of 64 floats (3.07 GB).
+    S, W, d = BIG_S, 64, 64
+    _say("f32 prefill beyond 2 GiB per head", S, W)
+    q, k, v = apex_inputs.prefill_inputs(1, S, 1, 1, d, "f32", seed=94, device="cuda")
+    o, kr = torch.empty_like(q), torch.empty_like(k)
+    taa.apex_attn_prefill(q, k, v, o, kr, causal=1, W=W, apply_rope=1)
+    torch.cuda.synchronize()
+    stats = _Stats()
+    for c in (100, (1 << 23) - 1, 1 << 23, (1 << 23) + 1, S - 1):
+        lo, hi = max(0, c - 255), min(S, c + 129)
+        ref = oracle.prefill(q[:, :, lo:hi].cpu(), k[:, :, lo:hi].cpu(), v[:, :, lo:hi].cpu(),
+                             causal=1, W=W, m0=lo)
+        first = 0 if lo == 0 else W - 1
+        stats.add(o[:, :, lo + first:hi], ref[:, :, first:], "rows %d..%d" % (lo + first, hi - 1))
+    stats.check("f32", "f32 prefill S=%d W=%d around byte offset 2**31" % (S, W))
+
+
 @pytest.mark.parametrize("m", [(1 << 23) + 10, BIG_S - 1])
 def test_decode_slots_beyond_2_gib_in_one_head(taa, m):
     # A cache of 12e6 slots per (b, KV head); with a 64-slot window the visible
@@ -847,6 +891,19 @@ def test_workload_rmsnorm(taa, name):
     torch.cuda.synchronize()
     ref = oracle.rmsnorm(x.cpu(), g.cpu(), eps=w["eps"])
     _check_rmsnorm(y, ref, w["dtype"], name)
+
+
+def test_rmsnorm_beyond_2g_elements(taa):
+    # 300,000 rows of 8192 bf16 features: 2.46e9 elements (4.9 GB), rows from
+    # 262,144 on starting past element 2**31.
+    rows, d = 300_000, 8192
+    _say("rmsnorm beyond 2**31 elements", rows, d)
+    x, g = apex_inputs.rmsnorm_inputs(1, rows, d, "bf16", seed=95, device="cuda")
+    y = taa.apex_rmsnorm(x, g, eps=1e-6)
+    torch.cuda.synchronize()
+    pick = torch.tensor([0, 1, (1 << 18) - 1, 1 << 18, (1 << 18) + 1, 280_001, rows - 1])
+    ref = oracle.rmsnorm(x[0, pick.cuda()].cpu(), g.cpu(), eps=1e-6)
+    _check_rmsnorm(y[0, pick.cuda()], ref, "bf16", "rmsnorm rows %s of %d" % (pick.tolist(), rows))
 
 
 def test_calls_replay_from_a_hip_graph(taa):
