@@ -144,6 +144,11 @@ PREFILL_CASES = [
     (1, 77, 4, 1, 128, 1, 9, 5, "f32", 1),
     (2, 33, 2, 2, 64, 0, 0, 0, "f32", 1),
     (1, 300, 8, 2, 128, 1, 0, 0, "f32", 0),
+    # many batch elements of a short sequence: the flat work-item index of the
+    # bf16 prefill and the batch grid dimension of the fp32 one
+    (1500, 3, 8, 2, 128, 1, 0, 0, "bf16", 1),
+    (700, 5, 4, 4, 64, 1, 2, 11, "bf16", 1),
+    (1200, 2, 4, 1, 64, 1, 0, 0, "f32", 1),
 ]
 
 
@@ -589,6 +594,9 @@ DECODE_CASES = [
     (1, 5000, 64, 2, 128, 0, 4321, True, 1),
     (3, 4096, 12, 4, 64, 100, 4095, True, 1),
     (2, 20000, 16, 1, 128, 0, 19999, True, 1),
+    # many batch elements of a short cache (the batch grid dimension)
+    (2000, 40, 16, 2, 128, 0, 39, True, 1),
+    (3000, 64, 8, 8, 64, 16, 50, True, 1),
 ]
 
 
