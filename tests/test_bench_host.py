@@ -67,3 +67,34 @@ def test_cpu_baseline_sample_counts_its_rows():
     whole = bench.prefill_flops(w)
     assert 4 * w["d"] * G * bench.n_visible(w["S"], w["causal"], w["W"]) * w["B"] * w["Hkv"] \
         == whole
+
+
+def test_prefill_roofline_block_carries_the_contract_fields():
+    import apex_inputs
+    w = apex_inputs.WORKLOADS[bench.HEADLINE]
+    r = bench.prefill_roofline(w, 1.6, bench.PREFILL_KERNEL, bench.HEADLINE)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2516.6
+    assert r["achieved"] == round(bench.prefill_flops(w) / 1.6e-3 / 1e12, 1)
+    assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-4
+    assert r["algorithmic_bytes"] == bench.prefill_bytes(w)
+
+
+@pytest.mark.parametrize("workload,kernel", [
+    ("window_prefill_s16384_w4096", "PREFILL_KERNEL"),
+    ("gqa_prefill_s2048", "PREFILL_KERNEL"),
+    ("local_prefill_s65536_w512", "PREFILL_KERNEL"),
+    ("gqa_decode_sk32768", "DECODE_KERNEL"),
+])
+def test_committed_traffic_matches_the_kernel_sources(workload, kernel):
+    # the counter-derived HBM bytes under profiles/ were taken with the kernel
+    # sources as they are now (else the bench reports traffic as null)
+    t = bench.load_traffic(workload, getattr(bench, kernel))
+    assert t is not None and t > 0
+
+
+def test_cpu_baseline_block_fields():
+    import apex_inputs
+    w = dict(apex_inputs.WORKLOADS[bench.HEADLINE], S=256, W=64)
+    c = bench.cpu_baseline(w, 0.0)
+    assert c["kind"] == "oracle" and c["unit"] == "TFLOP/s" and c["cores"] >= 1
+    assert c["value"] > 0 and "1 whole pass" in c["sample"]
