@@ -294,3 +294,53 @@ def test_misaligned_pointers_are_rejected(L):
         assert _decode_mla(L, **{name: off}) == EINVAL, name
     for name in ("x", "g", "y"):
         assert _rms(L, **{name: off}) == EINVAL, name
+
+
+def test_binding_checks_shapes_before_any_pointer():
+    # the C entry points take sizes once and touch every buffer to the extent
+    # they imply, so the binding refuses tensors that do not match the call
+    import torch
+    import transformer_attention_amd as taa
+    bf = torch.bfloat16
+    q = torch.zeros(1, 4, 8, 64, dtype=bf)
+    k = torch.zeros(1, 2, 8, 64, dtype=bf)
+    o = torch.zeros(1, 4, 8, 64, dtype=bf)
+    bad = [
+        dict(k=torch.zeros(1, 2, 9, 64, dtype=bf)),               # S differs from q's
+        dict(v=torch.zeros(1, 2, 8, 32, dtype=bf)),               # d differs
+        dict(o=torch.zeros(1, 2, 8, 64, dtype=bf)),               # o with H_kv heads
+        dict(k_rope_out=torch.zeros(1, 4, 8, 64, dtype=bf)),      # rotated k with H_q heads
+        dict(v=torch.zeros(1, 2, 8, 64, dtype=torch.float32)),    # dtype differs
+        dict(k=torch.zeros(2, 8, 64, dtype=bf)),                  # not [B, H, S, d]
+    ]
+    for change in bad:
+        args = dict(q=q, k=k, v=k.clone(), o=o, k_rope_out=None)
+        args.update(change)
+        with pytest.raises(ValueError, match="apex_attn_prefill"):
+            taa.apex_attn_prefill(**args)
+    with pytest.raises(ValueError, match="device tensors"):  # consistent: reaches the device check
+        taa.apex_attn_prefill(q, k, k.clone(), o, k.clone())
+
+    qd = torch.zeros(2, 16, 1, 64, dtype=bf)
+    kc = torch.zeros(2, 1, 100, 64, dtype=bf)
+    kn = torch.zeros(2, 1, 1, 64, dtype=bf)
+    od = torch.zeros(2, 16, 1, 64, dtype=bf)
+    for fn in (taa.apex_attn_decode, taa.apex_attn_decode_noalloc):
+        with pytest.raises(ValueError, match="v_cache"):
+            fn(qd, kc, torch.zeros(2, 1, 99, 64, dtype=bf), kn, kn.clone(), od, m=99)
+        with pytest.raises(ValueError, match="k_new"):
+            fn(qd, kc, kc.clone(), torch.zeros(2, 2, 1, 64, dtype=bf), kn, od, m=99)
+        with pytest.raises(ValueError, match="o has shape"):
+            fn(qd, kc, kc.clone(), kn, kn.clone(), torch.zeros(2, 16, 1, 32, dtype=bf), m=99)
+    x = torch.zeros(3, 64, dtype=bf)
+    with pytest.raises(ValueError, match="gamma"):
+        taa.apex_rmsnorm(x, torch.ones(32, dtype=bf))
+    with pytest.raises(ValueError, match="y has shape"):
+        taa.apex_rmsnorm(x, torch.ones(64, dtype=bf), torch.zeros(3, 32, dtype=bf))
+    with pytest.raises(ValueError, match="k_out"):
+        taa.apex_rope_qk(q, k, None, torch.zeros(1, 2, 8, 32, dtype=bf))
+    mq = torch.zeros(1, 4, 8, 192, dtype=bf)
+    mk = torch.zeros(1, 2, 8, 192, dtype=bf)
+    with pytest.raises(ValueError, match="o has shape"):
+        taa.apex_attn_prefill_mla(mq, mk, torch.zeros(1, 2, 8, 128, dtype=bf),
+                                  torch.zeros(1, 4, 8, 192, dtype=bf))

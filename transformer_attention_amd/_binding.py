@@ -85,6 +85,26 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _expect(fn, name, t, shape, like):
+    """The C entry points take sizes once and read or write every buffer to
+    the extent those sizes imply, so each tensor must have exactly the shape
+    (and the dtype and device of `like`) that the call describes."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: %s has shape %s, the call needs %s"
+                         % (fn, name, tuple(t.shape), tuple(shape)))
+    if t.dtype != like.dtype or t.device != like.device:
+        raise ValueError("%s: %s is %s on %s, the call needs %s on %s"
+                         % (fn, name, t.dtype, t.device, like.dtype, like.device))
+
+
+def _dims4(fn, name, t):
+    if t.dim() != 4:
+        raise ValueError("%s: %s must be a [B, H, S, d] tensor, got %d dims" % (fn, name, t.dim()))
+    return tuple(t.shape)
+
+
 def _stream(t, stream):
     if stream is not None:
         return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -104,9 +124,12 @@ def apex_rope_qk(q, k, q_out=None, k_out=None, m0=0, base=10000.0, stream=None, 
     if k is not None and k_out is None:
         k_out = k
     t = q if q is not None else k
-    B, _, S, d = t.shape
+    B, _, S, d = _dims4("apex_rope_qk", "q" if q is not None else "k", t)
     Hq = q.shape[1] if q is not None else 0
-    Hkv = k.shape[1] if k is not None else 0
+    Hkv = _dims4("apex_rope_qk", "k", k)[1] if k is not None else 0
+    _expect("apex_rope_qk", "q_out", q_out, (B, Hq, S, d), t)
+    _expect("apex_rope_qk", "k", k, (B, Hkv, S, d), t)
+    _expect("apex_rope_qk", "k_out", k_out, (B, Hkv, S, d), t)
     _check("apex_rope_qk", lib().apex_rope_qk(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), B, S,
                                               Hq, Hkv, d, int(m0), float(base), float(yarn_s),
                                               _dtype_code(t), _stream(t, stream)))
@@ -118,8 +141,13 @@ def apex_attn_prefill(q, k, v, o, k_rope_out=None, causal=1, W=0, m0=0, base=100
     (RoPE(k) lands in k_rope_out), 2 = rotate q only (k holds rotated keys), 0 = none.
     prefix: rows i < prefix see exactly the keys j < prefix (bidirectional prefix).
     yarn_s: YaRN scale factor (frequencies, and the score temperature when > 1)."""
-    B, Hq, S, d = q.shape
-    Hkv = k.shape[1]
+    fn = "apex_attn_prefill"
+    B, Hq, S, d = _dims4(fn, "q", q)
+    Hkv = _dims4(fn, "k", k)[1]
+    _expect(fn, "k", k, (B, Hkv, S, d), q)
+    _expect(fn, "v", v, (B, Hkv, S, d), q)
+    _expect(fn, "o", o, (B, Hq, S, d), q)
+    _expect(fn, "k_rope_out", k_rope_out, (B, Hkv, S, d), q)
     _check("apex_attn_prefill",
            lib().apex_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(k_rope_out), B, S, Hq,
                                    Hkv, d, int(causal), int(W), int(prefix), int(m0), float(base),
@@ -131,8 +159,13 @@ def apex_attn_prefill_mla(q, k, v, o, k_rope_out=None, causal=1, W=0, m0=0, base
                           apply_rope=1, stream=None, prefix=0, yarn_s=1.0):
     """MLA attention with decoupled RoPE: q, k rows are [content (d_h) | rope (d_r)],
     v and o rows d_h wide; d_r = q width - v width. Other arguments as apex_attn_prefill."""
-    B, Hq, S, dqk = q.shape
-    Hkv, d_h = k.shape[1], v.shape[3]
+    fn = "apex_attn_prefill_mla"
+    B, Hq, S, dqk = _dims4(fn, "q", q)
+    Hkv, d_h = _dims4(fn, "k", k)[1], _dims4(fn, "v", v)[3]
+    _expect(fn, "k", k, (B, Hkv, S, dqk), q)
+    _expect(fn, "v", v, (B, Hkv, S, d_h), q)
+    _expect(fn, "o", o, (B, Hq, S, d_h), q)
+    _expect(fn, "k_rope_out", k_rope_out, (B, Hkv, S, dqk), q)
     _check("apex_attn_prefill_mla",
            lib().apex_attn_prefill_mla(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(k_rope_out), B, S,
                                        Hq, Hkv, d_h, dqk - d_h, int(causal), int(W), int(prefix),
@@ -147,10 +180,23 @@ def apex_rmsnorm(x, gamma, y=None, eps=1e-6, stream=None):
         y = torch.empty_like(x)
     d = x.shape[-1]
     rows = x.numel() // d if d else 0
+    _expect("apex_rmsnorm", "gamma", gamma, (d,), x)
+    _expect("apex_rmsnorm", "y", y, tuple(x.shape), x)
     _check("apex_rmsnorm",
            lib().apex_rmsnorm(_ptr(x), _ptr(gamma), _ptr(y), rows, d, float(eps), _dtype_code(x),
                               _stream(x, stream)))
     return y
+
+
+def _check_decode_shapes(fn, q, k_cache, v_cache, k_new, v_new, o, dqk, dv):
+    B, Hq, _, _ = q.shape
+    _, Hkv, Sk, _ = k_cache.shape
+    _expect(fn, "q", q, (B, Hq, 1, dqk), q)
+    _expect(fn, "k_cache", k_cache, (B, Hkv, Sk, dqk), q)
+    _expect(fn, "v_cache", v_cache, (B, Hkv, Sk, dv), q)
+    _expect(fn, "k_new", k_new, (B, Hkv, 1, dqk), q)
+    _expect(fn, "v_new", v_new, (B, Hkv, 1, dv), q)
+    _expect(fn, "o", o, (B, Hq, 1, dv), q)
 
 
 def apex_attn_decode_workspace_bytes(B, H_q, H_kv, Sk, d_h):
@@ -160,8 +206,10 @@ def apex_attn_decode_workspace_bytes(B, H_q, H_kv, Sk, d_h):
 def apex_attn_decode(q, k_cache, v_cache, k_new, v_new, o, m, W=0, base=10000.0, apply_rope=1,
                      workspace=None, stream=None, yarn_s=1.0):
     """One query per (b, h) at position m against [B,H_kv,Sk,d_h] caches."""
-    B, Hq, _, d = q.shape
-    Hkv, Sk = k_cache.shape[1], k_cache.shape[2]
+    fn = "apex_attn_decode"
+    B, Hq, _, d = _dims4(fn, "q", q)
+    _, Hkv, Sk, _ = _dims4(fn, "k_cache", k_cache)
+    _check_decode_shapes(fn, q, k_cache, v_cache, k_new, v_new, o, d, d)
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("apex_attn_decode",
            lib().apex_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
@@ -174,8 +222,10 @@ def apex_attn_decode(q, k_cache, v_cache, k_new, v_new, o, m, W=0, base=10000.0,
 def apex_attn_decode_noalloc(q, k_cache, v_cache, k_new, v_new, o, m, W=0, base=10000.0,
                              apply_rope=1, stream=None, yarn_s=1.0):
     """apex_attn_decode with the library's own scratch instead of a workspace."""
-    B, Hq, _, d = q.shape
-    Hkv, Sk = k_cache.shape[1], k_cache.shape[2]
+    fn = "apex_attn_decode_noalloc"
+    B, Hq, _, d = _dims4(fn, "q", q)
+    _, Hkv, Sk, _ = _dims4(fn, "k_cache", k_cache)
+    _check_decode_shapes(fn, q, k_cache, v_cache, k_new, v_new, o, d, d)
     _check("apex_attn_decode_noalloc",
            lib().apex_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new),
                                           _ptr(v_new), _ptr(o), B, Sk, Hq, Hkv, d, int(W), int(m),
@@ -187,8 +237,11 @@ def apex_attn_decode_mla(q, k_cache, v_cache, k_new, v_new, o, m, W=0, base=1000
                          apply_rope=1, workspace=None, stream=None, yarn_s=1.0):
     """MLA decode: q [B,H_q,1,d_h+d_r], k_cache [B,H_kv,Sk,d_h+d_r] ([content | rope]),
     v_cache [B,H_kv,Sk,d_h]; d_r = q width - v width. Other arguments as apex_attn_decode."""
-    B, Hq, _, dqk = q.shape
-    Hkv, Sk, d_h = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    fn = "apex_attn_decode_mla"
+    B, Hq, _, dqk = _dims4(fn, "q", q)
+    _, Hkv, Sk, _ = _dims4(fn, "k_cache", k_cache)
+    d_h = _dims4(fn, "v_cache", v_cache)[3]
+    _check_decode_shapes(fn, q, k_cache, v_cache, k_new, v_new, o, dqk, d_h)
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("apex_attn_decode_mla",
            lib().apex_attn_decode_mla(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new),
