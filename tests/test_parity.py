@@ -914,6 +914,38 @@ def test_rmsnorm_beyond_2g_elements(taa):
     _check_rmsnorm(y[0, pick.cuda()], ref, "bf16", "rmsnorm rows %s of %d" % (pick.tolist(), rows))
 
 
+def test_calls_on_concurrent_streams_match_serial_calls(taa):
+    # Every entry point only enqueues work on the stream it is given and keeps
+    # no state between calls (the decode's partials live in the caller's
+    # workspace), so calls on different streams may overlap freely.
+    dev = torch.device("cuda")
+    q, k, v = apex_inputs.prefill_inputs(2, 700, 16, 4, 128, "bf16", seed=31, device=dev)
+    qd, kc, vc, kn, vn = apex_inputs.decode_inputs(8, 9000, 32, 2, 128, "bf16", seed=32,
+                                                   device=dev)
+    x, g = apex_inputs.rmsnorm_inputs(4, 3000, 4096, "bf16", seed=33, device=dev)
+    ws = torch.empty(taa.apex_attn_decode_workspace_bytes(8, 32, 2, 9000, 128),
+                     dtype=torch.uint8, device=dev)
+
+    def run(streams):
+        o, kr = torch.empty_like(q), torch.empty_like(k)
+        od = torch.empty_like(qd)
+        kc1, vc1 = kc.clone(), vc.clone()
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        taa.apex_attn_prefill(q, k, v, o, kr, causal=1, W=300, stream=streams[0])
+        taa.apex_attn_decode(qd, kc1, vc1, kn, vn, od, m=8999, workspace=ws, stream=streams[1])
+        taa.apex_rmsnorm(x, g, y, stream=streams[2])
+        torch.cuda.synchronize()
+        return o, kr, od, kc1, y
+
+    serial = run([torch.cuda.current_stream()] * 3)
+    side = [torch.cuda.Stream(device=dev) for _ in range(3)]  # default priority
+    for _ in range(3):
+        together = run(side)
+        for a, b in zip(serial, together):
+            assert torch.equal(a, b)
+
+
 def test_calls_replay_from_a_hip_graph(taa):
     # Every entry point only enqueues kernels on the caller's stream and
     # allocates nothing, so a sequence of calls can be captured once and
